@@ -1,0 +1,337 @@
+"""Pins for the oracle's routing, permutation, expert FFN and combine (CPU only).
+
+The oracle is checked against: library routines (numpy lexsort / argsort / bincount, scipy's
+softmax and logistic), closed forms built from permutation and one-hot expert weights, a dense
+brute-force MoE that never permutes rows, and invariants the layer must satisfy (gate weights
+sum to one, the permutation is a bijection, compact output plus the miss rows equals the
+all-resident output, token-permutation equivariance)."""
+import numpy as np
+import pytest
+from scipy import special
+
+from oracle import moe_oracle as O
+from synth import gen
+
+
+# ----------------------------------------------------------------------------------------------
+# helpers written independently of the oracle's own stage functions
+# ----------------------------------------------------------------------------------------------
+
+def lexsort_topk(l32, k):
+    T, E = l32.shape
+    out = np.empty((T, k), np.int64)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -l32[t].astype(np.float64)))
+        out[t] = order[:k]
+    return out
+
+
+def brute_force(inp, slot_map=None):
+    """Dense MoE: every expert evaluated on every token, masked by a [T,E] gate matrix."""
+    cfg = inp.cfg
+    x = O.activations_f64(inp.x, cfg.xdtype)
+    if inp.logits is None:
+        l32 = (x @ inp.w_router.astype(np.float64).T).astype(np.float32)
+    else:
+        l32 = inp.logits.astype(np.float32)
+    sel = lexsort_topk(l32, cfg.k)
+    l = l32.astype(np.float64)
+    s = special.softmax(l, axis=1) if cfg.score == "softmax" else special.expit(l)
+    G = np.zeros((cfg.T, cfg.E))
+    for t in range(cfg.T):
+        tot = s[t, sel[t]].sum()
+        for e in sel[t]:
+            if slot_map is None or slot_map[e] >= 0:
+                G[t, e] = s[t, e] / tot
+    out = np.zeros((cfg.T, cfg.H))
+    for e in range(cfg.E):
+        if not G[:, e].any():
+            continue
+        w_gu, s_gu, w_d, s_d = gen.expert_weights(cfg, e)
+        gu = O.dequant(cfg.wdtype, w_gu, s_gu, 2 * cfg.I, cfg.H)
+        wd = O.dequant(cfg.wdtype, w_d, s_d, cfg.H, cfg.I)
+        g = np.einsum("th,ih->ti", x, gu[: cfg.I])
+        u = np.einsum("th,ih->ti", x, gu[cfg.I:])
+        a = g * special.expit(g) * u
+        out += G[:, e:e + 1] * np.einsum("ti,hi->th", a, wd)
+    return out, sel
+
+
+def run_oracle(inp, **kw):
+    cfg = inp.cfg
+    return O.layer(inp.x, cfg.xdtype, inp.weights, cfg.wdtype, cfg.H, cfg.I, cfg.E, cfg.k,
+                   cfg.score, cfg.renorm, w_router=inp.w_router, logits=inp.logits,
+                   bias=inp.bias, slot_map=inp.slot_map, S=cfg.S, **kw)
+
+
+SHRUNK = {
+    "tiny": gen.config("tiny"),
+    "bf16": gen.config("decode_bf16", T=5, H=256, E=16, I=128, k=4),
+    "fp8": gen.config("decode_fp8", T=9, H=384, E=12, I=256, k=3),
+    "fp8_zipf": gen.config("prefill_fp8_zipf", T=24, H=256, E=16, I=128, k=4),
+    "mxfp4_compact": gen.config("compact_mxfp4", T=12, H=256, E=16, I=128, k=4, resident=6),
+}
+
+
+# ----------------------------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------------------------
+
+def test_select_topk_matches_lexsort():
+    rng = np.random.default_rng(1)
+    l = rng.standard_normal((50, 40)).astype(np.float32)
+    l[:, 7] = l[:, 3]                      # exact ties: the smaller id must come first
+    l[5, :] = 0.25                         # a fully tied token
+    assert np.array_equal(O.select_topk(l, 6), lexsort_topk(l, 6))
+    assert list(O.select_topk(l, 6)[5]) == [0, 1, 2, 3, 4, 5]
+
+
+def test_softmax_renorm_is_softmax_of_selected_logits():
+    rng = np.random.default_rng(2)
+    l = (rng.standard_normal((20, 8)) * 3).astype(np.float32)
+    idx, w, _ = O.route(l, 2, "softmax")
+    picked = np.take_along_axis(l.astype(np.float64), idx.astype(np.int64), axis=1)
+    np.testing.assert_allclose(w, special.softmax(picked, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-14)
+
+
+def test_sigmoid_renorm_matches_expit():
+    rng = np.random.default_rng(3)
+    l = (rng.standard_normal((20, 64)) * 4).astype(np.float32)
+    idx, w, _ = O.route(l, 8, "sigmoid")
+    p = special.expit(np.take_along_axis(l.astype(np.float64), idx.astype(np.int64), axis=1))
+    np.testing.assert_allclose(w, p / p.sum(axis=1, keepdims=True), rtol=1e-13)
+    # without renormalisation the gates are the raw scores
+    _, w_raw, _ = O.route(l, 8, "sigmoid", renorm=False)
+    np.testing.assert_allclose(w_raw, p, rtol=1e-13)
+
+
+def test_selection_order_is_descending_score():
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal((30, 32)).astype(np.float32)
+    idx, w, _ = O.route(l, 5, "sigmoid")
+    assert np.all(np.diff(w, axis=1) <= 0)
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1])   # distinct
+
+
+def test_bias_shifts_selection():
+    l = np.zeros((1, 6), np.float32)
+    bias = np.array([0, 0, 0, 0, 5, 3], np.float32)
+    idx, w, _ = O.route(l, 2, "sigmoid", bias=bias)
+    assert list(idx[0]) == [4, 5]
+    p = special.expit(np.array([5.0, 3.0]))
+    np.testing.assert_allclose(w[0], p / p.sum(), rtol=1e-14)
+
+
+def test_near_tie_flags():
+    l = np.array([[3.0, 2.0, 1.0, 0.0], [3.0, 2.0, 2.0 + 1e-6, 0.0], [3.0, 2.0, 1.0, 1.0]],
+                 np.float32)
+    _, _, tie = O.route(l, 2, "sigmoid")
+    assert list(tie) == [False, True, False]      # token 2 ties below the (k+1)-th place only
+    _, _, tie3 = O.route(l, 3, "sigmoid")
+    assert list(tie3) == [False, True, True]
+
+
+def test_zipf_logits_give_skewed_groups():
+    cfg = gen.config("prefill_fp8_zipf", T=2048)
+    l = gen.make_logits(cfg)
+    idx = O.select_topk(l[:512], 8)
+    c = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    assert c.max() > 20 * max(1, np.median(c)) / 4 and (c == 0).sum() > 0
+    assert abs(gen.harmonic(384, 1.1) - 5.0699) < 1e-3
+
+
+# ----------------------------------------------------------------------------------------------
+# histogram / permutation / misses
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("compact", [False, True])
+def test_permutation_matches_stable_argsort(compact):
+    rng = np.random.default_rng(5)
+    T, E, k = 37, 20, 4
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k))
+    sm = None
+    S = E
+    if compact:
+        S = 7
+        sm = np.full(E, -1, np.int32)
+        sm[rng.permutation(E)[:S]] = np.arange(S)
+    counts = O.histogram(idx, E)
+    assert np.array_equal(counts, np.bincount(idx.reshape(-1), minlength=E))
+    assert counts.sum() == T * k
+    off, perm, inv = O.permute(idx, sm, S)
+    slot = idx.reshape(-1) if sm is None else sm[idx.reshape(-1)]
+    r = np.arange(T * k)
+    res = slot >= 0
+    key = slot[res].astype(np.int64) * (T * k) + r[res]
+    assert np.array_equal(perm, r[res][np.argsort(key, kind="stable")])
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(slot[res], minlength=S))]))
+    assert np.all(np.diff(off) >= 0)
+    assert np.array_equal(inv[perm], np.arange(perm.size))              # inverse
+    assert np.array_equal(np.sort(perm), r[res])                        # bijection onto residents
+    assert np.all(inv[~res] == -1)
+    mt, me, mw = O.miss_list(idx, w, sm)
+    assert perm.size + mt.size == T * k
+    assert np.array_equal(mt * k + (np.nonzero(~res)[0] % k), np.nonzero(~res)[0])
+    assert np.array_equal(me, idx.reshape(-1)[~res])
+    assert np.array_equal(mw, w.reshape(-1)[~res])
+
+
+# ----------------------------------------------------------------------------------------------
+# expert FFN closed forms
+# ----------------------------------------------------------------------------------------------
+
+def _perm_weights(wdtype, E, n, betas, s1, s2, s3):
+    """W_g = P(s1), W_u = beta_e P(s2), W_d = P(s3) stored in ``wdtype``; P(s)[i, s[i]] = 1."""
+    P = lambda s: np.eye(n)[s]
+    w_gu, s_gu, w_d, s_d = [], [], [], []
+    for e in range(E):
+        b = betas[e]
+        if wdtype == "f32":
+            w_gu.append(np.vstack([P(s1), b * P(s2)]).astype(np.float32))
+            w_d.append(P(s3).astype(np.float32))
+        elif wdtype == "bf16":
+            one = lambda M, v: np.where(M > 0, gen.f32_to_bf16_bits(np.float32(v)), 0).astype(np.uint16)
+            w_gu.append(np.vstack([one(P(s1), 1.0), one(P(s2), b)]))
+            w_d.append(one(P(s3), 1.0))
+        elif wdtype == "fp8":                                   # code 0x38 = 1.0, scale per block
+            c = lambda M: np.where(M > 0, 0x38, 0).astype(np.uint8)
+            w_gu.append(np.vstack([c(P(s1)), c(P(s2))]))
+            s_gu.append(np.array([[1.0], [b]], np.float32))
+            w_d.append(c(P(s3)))
+            s_d.append(np.array([[1.0]], np.float32))
+        elif wdtype == "mxfp4":                                 # code 0x2 = 1.0, e8m0 scale
+            def pk(M):
+                codes = np.where(M > 0, 2, 0).astype(np.uint8)
+                return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+            w_gu.append(np.vstack([pk(P(s1)), pk(P(s2))]))
+            sc = np.full((2 * n, n // 32), 127, np.uint8)
+            sc[n:] = 127 + int(np.log2(b))
+            s_gu.append(sc)
+            w_d.append(pk(P(s3)))
+            s_d.append(np.full((n, n // 32), 127, np.uint8))
+    st = lambda a: np.stack(a) if a else None
+    return dict(w_gu=st(w_gu), s_gu=st(s_gu), w_d=st(w_d), s_d=st(s_d))
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "fp8", "mxfp4"])
+def test_ffn_closed_form_with_permutation_weights(wdtype):
+    n, E, k, T = 128, 6, 3, 10
+    rng = np.random.default_rng(6)
+    s1, s2, s3 = rng.permutation(n), rng.permutation(n), rng.permutation(n)
+    betas = [1.0, 2.0, 4.0, 2.0, 1.0, 4.0]
+    W = _perm_weights(wdtype, E, n, betas, s1, s2, s3)
+    x = rng.standard_normal((T, n)).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    res = O.layer(x, "f32", W, wdtype, n, n, E, k, "sigmoid", logits=logits)
+    silu_x = x.astype(np.float64) * special.expit(x.astype(np.float64))
+    # y_h = silu(x[s1[s3[h]]]) * beta * x[s2[s3[h]]]
+    base = silu_x[:, s1[s3]] * x.astype(np.float64)[:, s2[s3]]
+    sel = lexsort_topk(logits, k)
+    p = special.expit(np.take_along_axis(logits.astype(np.float64), sel, axis=1))
+    gain = (p / p.sum(axis=1, keepdims=True) * np.array(betas)[sel]).sum(axis=1)
+    np.testing.assert_allclose(res["out"], base * gain[:, None], rtol=1e-12, atol=1e-300)
+
+
+def test_silu_reference_values():
+    # e/(1+e) and -1/(1+e): logistic function values at +-1
+    np.testing.assert_allclose(O.silu(np.array([1.0, -1.0, 0.0])),
+                               [0.7310585786300049, -0.2689414213699951, 0.0], rtol=1e-15)
+
+
+def test_single_expert_is_dense_swiglu():
+    cfg = gen.config("tiny", E=1, k=1)
+    inp = gen.make_inputs(cfg)
+    res = run_oracle(inp)
+    x = inp.x.astype(np.float64)
+    w_gu, w_d = inp.weights["w_gu"][0].astype(np.float64), inp.weights["w_d"][0].astype(np.float64)
+    g, u = x @ w_gu[: cfg.I].T, x @ w_gu[cfg.I:].T
+    ref = (special.expit(g) * g * u) @ w_d.T
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    assert np.all(res["topk_w"] == 1.0)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    cfg = gen.config("decode_bf16", T=6, H=256, E=10, I=128, k=3)
+    inp = gen.make_inputs(cfg)
+    one = gen.expert_weights(cfg, 0)
+    for i, key in enumerate(("w_gu", "s_gu", "w_d", "s_d")):
+        if inp.weights[key] is not None:
+            inp.weights[key][:] = one[i]
+    res = run_oracle(inp)
+    single = O.layer(inp.x, "bf16", {k_: (None if v is None else v[:1]) for k_, v in inp.weights.items()},
+                     "bf16", cfg.H, cfg.I, 1, 1, "sigmoid", logits=np.zeros((cfg.T, 1), np.float32))
+    np.testing.assert_allclose(res["out"], single["out"], rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SHRUNK))
+def test_layer_matches_dense_brute_force(name):
+    cfg = SHRUNK[name]
+    inp = gen.make_inputs(cfg)
+    res = run_oracle(inp)
+    ref, sel = brute_force(inp, inp.slot_map)
+    assert np.array_equal(res["topk_idx"], sel)
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+    np.testing.assert_allclose(res["topk_w"].sum(axis=1), 1.0, rtol=1e-14)
+
+
+def test_compact_plus_misses_equals_all_resident():
+    cfg = SHRUNK["mxfp4_compact"]
+    inp = gen.make_inputs(cfg)
+    compact = run_oracle(inp)
+    full_w = gen.stack_weights(cfg, range(cfg.E))
+    full = O.layer(inp.x, cfg.xdtype, full_w, cfg.wdtype, cfg.H, cfg.I, cfg.E, cfg.k, cfg.score,
+                   logits=inp.logits)
+    assert compact["miss_token"].size > 0 and compact["perm"].size > 0
+    x64 = O.activations_f64(inp.x, cfg.xdtype)
+    rebuilt = compact["out"].copy()
+    for t, e, w in zip(compact["miss_token"], compact["miss_expert"], compact["miss_weight"]):
+        wg, wu, wd = O.slot_matrices(full_w, cfg.wdtype, int(e), cfg.H, cfg.I)
+        rebuilt[t] += w * O.ffn(x64[t:t + 1], wg, wu, wd)[0]
+    np.testing.assert_allclose(rebuilt, full["out"], rtol=1e-12, atol=1e-15)
+    # resident rows + misses = all rows, and the per-expert counts agree with the full layer
+    assert compact["perm"].size + compact["miss_token"].size == cfg.T * cfg.k
+    assert np.array_equal(compact["counts"], full["counts"])
+
+
+def test_token_permutation_equivariance():
+    cfg = SHRUNK["fp8"]
+    inp = gen.make_inputs(cfg)
+    res = run_oracle(inp)
+    p = np.random.default_rng(7).permutation(cfg.T)
+    inp.x = inp.x[p]
+    inp.logits = inp.logits[p]
+    res2 = run_oracle(inp)
+    np.testing.assert_allclose(res2["out"], res["out"][p], rtol=1e-12, atol=1e-15)
+    assert np.array_equal(res2["topk_idx"], res["topk_idx"][p])
+
+
+def test_token_sample_matches_full_run():
+    cfg = SHRUNK["fp8_zipf"]
+    inp = gen.make_inputs(cfg)
+    full = run_oracle(inp)
+    toks = np.array([0, 5, 17, 23])
+    part = run_oracle(inp, tokens=toks)
+    np.testing.assert_allclose(part["out"], full["out"][toks], rtol=1e-12, atol=1e-15)
+
+
+def test_mode_b_mirror_error_is_small_but_nonzero():
+    cfg = SHRUNK["fp8"]
+    inp = gen.make_inputs(cfg)
+    a = run_oracle(inp)
+    b = run_oracle(inp, act_quant=O.act_quant_mx_e4m3)
+    rel = np.linalg.norm(b["out"] - a["out"]) / np.linalg.norm(a["out"])
+    assert 1e-4 < rel < 0.1
+
+
+def test_empty_tokens():
+    cfg = gen.config("tiny", T=0)
+    inp = gen.make_inputs(cfg)
+    res = run_oracle(inp)
+    assert res["out"].shape == (0, cfg.H) and res["perm"].size == 0
+    assert np.array_equal(res["slot_offsets"], np.zeros(cfg.E + 1))

@@ -1,0 +1,209 @@
+/*
+ * moe.h -- C ABI of the routed Mixture-of-Experts FFN layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (vLLM-Moet README: a Mixture-of-Experts layer with 384 routed experts, a resident
+ * subset of expert slots on the GPU and "compact" calls whose rows for absent experts are
+ * computed by another tier -- MoET hybrid table, rows "identity" and "footprint, power"):
+ *
+ *   logits  l[t,e]  = x[t,:] . W_r[e,:]            fp32 (+ bias[e], fp32)
+ *   top-k   e_tj    = k largest logits of token t, ties to the smaller expert id, j = 0..k-1
+ *                     in descending order
+ *   gates   w_tj    = s(e_tj) / sum_i s(e_ti)      s = softmax over all E, or sigmoid
+ *   FFN_e(x)        = W_d,e ( silu(W_g,e x) * (W_u,e x) ),  silu(z) = z / (1 + e^-z)
+ *   out[t]          = sum_{j: slot(e_tj) >= 0} w_tj FFN_{e_tj}(x[t])
+ *
+ * Rows r = t*k + j whose expert has no resident slot are not computed; they are returned as a
+ * (token, expert, weight) list in ascending r for another tier to add.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument named as device memory must be device memory of the current HIP
+ *     device; the caller owns it.  The library never allocates, frees or synchronises (except
+ *     moe_check_device_error, which says so).  Work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the null stream) in call order.
+ *   - Arguments are validated on the host before any HIP call.  A failing call returns a
+ *     non-zero moe_status, enqueues nothing, and leaves a message for moe_last_error().
+ *   - Matrices are row-major.  Weights are stored per slot as [N, K] with K (the input
+ *     dimension) contiguous: w_gu [S, 2I, H] (rows [0, I) gate, rows [I, 2I) up) and
+ *     w_d [S, H, I].
+ *   - Device pointers to weights, activations and outputs must be 16-byte aligned, workspaces
+ *     256-byte aligned.
+ *   - T = 0 is valid: nothing is enqueued.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* a NULL, negative, inconsistent or misaligned argument        */
+  MOE_ERR_UNSUPPORTED = 2,  /* a well-formed request outside what the kernels implement     */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes below the matching *_workspace_size()               */
+  MOE_ERR_HIP = 4,          /* a HIP launch or runtime call failed                          */
+  MOE_ERR_DEVICE = 5        /* a device-side check failed (see moe_check_device_error)      */
+} moe_status;
+
+/* Element formats.  Activation buffers use MOE_F32 or MOE_BF16 only. */
+typedef enum moe_dtype {
+  MOE_F32 = 0,           /* IEEE binary32                                                    */
+  MOE_BF16 = 1,          /* bfloat16 (upper half of a binary32)                              */
+  MOE_FP8_E4M3_B128 = 2, /* OCP FP8 E4M3 ("fn": bias 7, max 448, no inf) codes, one byte per
+                            weight; scales fp32 [S, ceil(N/128), ceil(K/128)], the value of
+                            w[n,k] is code * scale[n/128][k/128]                              */
+  MOE_MXFP4 = 3          /* OCP MX FP4: E2M1 codes, two per byte (K index 2j in the low nibble
+                            of byte j, 2j+1 in the high nibble); scales E8M0 uint8
+                            [S, N, K/32], value = e2m1 * 2^(scale - 127)                      */
+} moe_dtype;
+
+typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* Expert-FFN implementation: AUTO picks GEMV when few rows share a slot (T*k <= 4*S). */
+typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 } moe_path;
+
+/* Expert-FFN arithmetic.  MODE_A: activations kept in bf16/fp32, weights decoded exactly,
+ * fp32 accumulation.  MODE_B (GEMM path only): activations quantised per row and per 32
+ * K-elements to E4M3 with an E8M0 scale 2^(floor(log2 amax) - 8), saturating at +-448, before
+ * each projection, then low-precision MFMA. */
+typedef enum moe_mode { MOE_MODE_A = 0, MOE_MODE_B = 1 } moe_mode;
+
+/* The expert weights of one layer, in device memory.  S = number of slots, H = hidden size,
+ * I = expert intermediate size.  s_gu / s_d are NULL for MOE_F32 and MOE_BF16. */
+typedef struct moe_weights {
+  int wdtype; /* moe_dtype */
+  int S, H, I;
+  const void* w_gu; /* [S, 2I, H]; MXFP4: [S, 2I, H/2] bytes                         */
+  const void* s_gu; /* FP8: float [S, ceil(2I/128), ceil(H/128)]; MXFP4: [S, 2I, H/32] */
+  const void* w_d;  /* [S, H, I];  MXFP4: [S, H, I/2] bytes                           */
+  const void* s_d;  /* FP8: float [S, ceil(H/128), ceil(I/128)];  MXFP4: [S, H, I/32]  */
+} moe_weights;
+
+/* Routing configuration.  1 <= k <= min(E, 64), E <= 1024. */
+typedef struct moe_routing {
+  int E;      /* number of routed experts                                  */
+  int k;      /* experts per token                                         */
+  int score;  /* moe_score                                                 */
+  int renorm; /* non-zero: gates divided by the sum of the k chosen scores */
+} moe_routing;
+
+/* ------------------------------------------------------------------------------------------
+ * moe_route -- router logits, top-k selection, scores and renormalised gates.
+ *
+ * Exactly one of w_router / logits is non-NULL.
+ *   x         device [T, H], x_dtype MOE_F32 or MOE_BF16; unused (may be NULL) with `logits`
+ *   w_router  device fp32 [E, H]: logits are computed as x . W_r^T, fp32 accumulation
+ *   logits    device fp32 [T, E]: logits handed in directly
+ *   bias      device fp32 [E] or NULL, added to the logits in fp32 before selection
+ *   topk_idx  device int32 [T, k] out: expert ids, descending logit, ties to the smaller id
+ *   topk_w    device fp32 [T, k] out: gates (renormalised if cfg->renorm)
+ *   logits_out device fp32 [T, E] out or NULL: with w_router, where the computed logits (+bias)
+ *             are stored; NULL keeps them in the workspace
+ *   ws        device workspace of moe_route_workspace_size() bytes (may be 0 bytes / NULL)
+ * ------------------------------------------------------------------------------------------ */
+size_t moe_route_workspace_size(int T, const moe_routing* cfg, int with_router_weights);
+int moe_route(const void* x, int x_dtype, int T, int H, const float* w_router,
+              const float* logits, const float* bias, const moe_routing* cfg, int32_t* topk_idx,
+              float* topk_w, float* logits_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_permute -- expert histogram, slot grouping and the compact miss list.
+ *
+ * Row r = t*k + j is resident if slot(e) >= 0, where slot(e) = slot_map[e] (slot_map device
+ * int32 [E], entries in [-1, S)) or slot(e) = e when slot_map is NULL (then S must equal E).
+ *   counts       device int32 [E] out: rows per expert, absent experts included
+ *   slot_offsets device int32 [S+1] out: slot s owns positions [off[s], off[s+1]); off[S] is
+ *                the number of resident rows n_res
+ *   perm         device int32 [T*k] out: perm[p] = r for p < n_res, ordered by (slot, r)
+ *   inv_perm     device int32 [T*k] out: position of row r, or -1 if r is not resident
+ *   miss_count   device int32 [1] out: number of non-resident rows (required with slot_map)
+ *   miss_token / miss_expert (int32) / miss_weight (fp32 = topk_w of the row): device [T*k]
+ *                out, the first miss_count entries hold the non-resident rows in ascending r.
+ *                Required with slot_map; ignored (may be NULL) without it.
+ *   topk_w       device fp32 [T, k]; needed only with slot_map.
+ * An expert id outside [0, E) or a slot_map entry outside [-1, S) drops that row (it is
+ * neither resident nor a miss, inv_perm = -1) and raises the workspace error word.
+ * ------------------------------------------------------------------------------------------ */
+size_t moe_permute_workspace_size(int T, const moe_routing* cfg, int S);
+int moe_permute(const int32_t* topk_idx, const float* topk_w, int T, const moe_routing* cfg,
+                const int32_t* slot_map, int S, int32_t* counts, int32_t* slot_offsets,
+                int32_t* perm, int32_t* inv_perm, int32_t* miss_count, int32_t* miss_token,
+                int32_t* miss_expert, float* miss_weight, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_expert_ffn -- y_perm[p] = FFN_{slot of p}(x[perm[p] / k]) for every resident position p.
+ *
+ *   w             weights descriptor (host struct, device pointers inside)
+ *   x             device [T, H], x_dtype MOE_F32 or MOE_BF16
+ *   perm, slot_offsets  as produced by moe_permute (device)
+ *   path          moe_path; mode moe_mode
+ *   y_perm        device fp32 [T*k, H] out; rows >= n_res untouched
+ *   ws            device workspace of moe_expert_ffn_workspace_size() bytes
+ * moe_expert_gate_up and moe_expert_down are its two halves: gate_up leaves
+ * a = silu(W_g x) * (W_u x) in the workspace, down reads it.  Call them in that order with the
+ * same workspace, weights, T, k, path and mode.
+ * Positions whose perm entry names a token outside [0, T) are skipped.
+ * ------------------------------------------------------------------------------------------ */
+size_t moe_expert_ffn_workspace_size(const moe_weights* w, int T, int k, int path, int mode);
+int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int k,
+                   const int32_t* perm, const int32_t* slot_offsets, int path, int mode,
+                   float* y_perm, void* ws, size_t ws_bytes, void* stream);
+int moe_expert_gate_up(const moe_weights* w, const void* x, int x_dtype, int T, int k,
+                       const int32_t* perm, const int32_t* slot_offsets, int path, int mode,
+                       void* ws, size_t ws_bytes, void* stream);
+int moe_expert_down(const moe_weights* w, int T, int k, const int32_t* slot_offsets, int path,
+                    int mode, float* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_combine -- out[t] = sum over j ascending of topk_w[t,j] * y_perm[inv_perm[t*k+j]],
+ * resident rows only, fp32 accumulation, then rounded (nearest-even) to out_dtype.  A token
+ * with no resident row gets a zero row.  H % 4 == 0.
+ *   y_perm device fp32 [>= n_res, H]; inv_perm device int32 [T*k]; topk_w device fp32 [T*k];
+ *   out device [T, H] of out_dtype (MOE_F32 or MOE_BF16).
+ * ------------------------------------------------------------------------------------------ */
+int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int k,
+                int H, void* out, int out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_layer -- route, permute, expert FFN and combine in one call, one workspace, no host
+ * synchronisation.
+ *   x, x_dtype, T, w_router / logits, bias, cfg   as moe_route (H = w->H)
+ *   slot_map      device int32 [E] or NULL (all resident, w->S == cfg->E)
+ *   w, path, mode as moe_expert_ffn
+ *   out           device [T, H] out, out_dtype MOE_F32 or MOE_BF16
+ *   topk_idx, topk_w  device [T, k] out, or NULL to keep them in the workspace
+ *   miss_*        as moe_permute (required with slot_map)
+ *   ws            device workspace of moe_layer_workspace_size() bytes; its first 256 bytes
+ *                 hold the device error word read by moe_check_device_error
+ * ------------------------------------------------------------------------------------------ */
+size_t moe_layer_workspace_size(int T, const moe_routing* cfg, const moe_weights* w, int path,
+                                int mode, int with_router_weights);
+int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const float* logits,
+              const float* bias, const moe_routing* cfg, const int32_t* slot_map,
+              const moe_weights* w, int path, int mode, void* out, int out_dtype,
+              int32_t* topk_idx, float* topk_w, int32_t* miss_count, int32_t* miss_token,
+              int32_t* miss_expert, float* miss_weight, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * helpers
+ * ------------------------------------------------------------------------------------------ */
+/* Reads the error word at the start of a moe_permute / moe_layer workspace: synchronises
+ * `stream`, returns MOE_OK, MOE_ERR_DEVICE (an out-of-range expert id or slot_map entry was
+ * seen) or MOE_ERR_HIP. */
+int moe_check_device_error(const void* ws, void* stream);
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+/* Message of the last failing call made by this thread ("" if none). */
+const char* moe_last_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,118 @@
+// Device helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// element formats (same values as the public moe_dtype)
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3 };
+
+// ---------------------------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// E8M0 scale code -> fp32 value 2^(c-127) (c = 0 gives the subnormal 2^-127, 255 NaN)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  c &= 0xFFu;
+  if (c == 0) return __uint_as_float(0x00400000u);
+  if (c == 255) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float(c << 23);
+}
+
+// two OCP e4m3fn codes (bytes 0,1 or 2,3 of w) -> fp32 (gfx950 converts the OCP format)
+__device__ __forceinline__ float2 fp8x2_lo(uint32_t w) {
+  auto v = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  return make_float2(v[0], v[1]);
+}
+__device__ __forceinline__ float2 fp8x2_hi(uint32_t w) {
+  auto v = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return make_float2(v[0], v[1]);
+}
+
+// two e2m1 codes (byte `sel` of w; low nibble first) -> fp32, each multiplied by `scale`
+template <int SEL>
+__device__ __forceinline__ float2 fp4x2(uint32_t w, float scale) {
+  auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
+  return make_float2(v[0], v[1]);
+}
+
+// 16-byte streaming load (non-temporal hint: weights are read once per call)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------------------------
+// wave-level reductions (64 lanes)
+// ---------------------------------------------------------------------------------------------
+template <int WIDTH = kWave>
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WIDTH);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------------------------------------
+// active-slot lookup: the ord-th slot with a non-empty row range in off[0..S]
+// (block-cooperative; every thread of the block gets the same answer, -1 if none)
+// ---------------------------------------------------------------------------------------------
+template <int BLOCK>
+__device__ int find_active_slot(const int32_t* __restrict__ off, int S, int ord, int* lds /*[BLOCK/64+1]*/) {
+  constexpr int NW = BLOCK / kWave;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int before = 0;  // active slots in earlier chunks
+  for (int base = 0; base < S; base += BLOCK) {
+    int s = base + tid;
+    bool act = false;
+    if (s < S) act = off[s + 1] > off[s];
+    unsigned long long m = __ballot(act);
+    if (lane == 0) lds[wid] = __popcll(m);
+    __syncthreads();
+    int wbase = before;
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      int c = lds[w];
+      if (w < wid) wbase += c;
+      total += c;
+    }
+    int rank = wbase + __popcll(m & ((1ull << lane) - 1ull));
+    __syncthreads();
+    if (act && rank == ord) lds[NW] = s;
+    if (ord < before + total) {
+      __syncthreads();
+      int r = lds[NW];
+      __syncthreads();
+      return r;
+    }
+    before += total;
+  }
+  return -1;
+}
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI (moe_abi.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router_logits(const void* x, int xdt, const float* wr, const float* bias,
+                                float* logits, int T, int H, int E, hipStream_t st);
+hipError_t launch_topk(const float* logits, const float* bias, int add_bias, int T, int E, int k,
+                       int score, int renorm, int32_t* idx, float* w, hipStream_t st);
+
+size_t permute_lds_bytes(int E, int S);
+hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
+                          const int32_t* slot_map, int S, int32_t* counts, int32_t* slot_offsets,
+                          int32_t* perm, int32_t* inv_perm, int32_t* miss_count,
+                          int32_t* miss_token, int32_t* miss_expert, float* miss_weight,
+                          uint32_t* err, hipStream_t st);
+
+struct GemvArgs {
+  int wdt, xdt;
+  int S, T, k, H, I;
+  int n_ord;  // grid rows: an upper bound on the number of non-empty slots
+  const void* w_gu;
+  const void* s_gu;
+  const void* w_d;
+  const void* s_d;
+  const void* x;
+  const int32_t* perm;
+  const int32_t* off;
+  float* a;  // [T*k, I] fp32
+  float* y;  // [T*k, H] fp32
+};
+hipError_t launch_gemv_gate_up(const GemvArgs& g, hipStream_t st);
+hipError_t launch_gemv_down(const GemvArgs& g, hipStream_t st);
+
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int T, int k, int H,
+                          void* out, int odt, hipStream_t st);
+
+}  // namespace moe

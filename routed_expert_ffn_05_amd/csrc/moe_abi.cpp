@@ -1,0 +1,429 @@
+// C ABI of the MoE layer: host-side validation (before any HIP call), workspace carving and
+// dispatch to the gfx950 kernels.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+constexpr int kMaxDim = 8192;
+constexpr long long kMaxRows = 1LL << 26;  // T*k
+
+int elems_per_chunk(int wdtype) {
+  switch (wdtype) {
+    case MOE_F32: return 4;
+    case MOE_BF16: return 8;
+    case MOE_FP8_E4M3_B128: return 16;
+    case MOE_MXFP4: return 32;
+  }
+  return 0;
+}
+
+int check_routing(const moe_routing* cfg) {
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->E < 1) return fail(MOE_ERR_INVALID_ARG, "E = %d must be >= 1", cfg->E);
+  if (cfg->E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E = %d above %d", cfg->E, kMaxE);
+  if (cfg->k < 1 || cfg->k > cfg->E)
+    return fail(MOE_ERR_INVALID_ARG, "k = %d must be in [1, E = %d]", cfg->k, cfg->E);
+  if (cfg->k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k = %d above %d", cfg->k, kMaxK);
+  if (cfg->score != MOE_SCORE_SOFTMAX && cfg->score != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "unknown score function %d", cfg->score);
+  return MOE_OK;
+}
+
+int check_T(int T, int k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((long long)T * k > kMaxRows) return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld above %lld", (long long)T * k, kMaxRows);
+  return MOE_OK;
+}
+
+int check_act_dtype(int dt, const char* what) {
+  if (dt != MOE_F32 && dt != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "%s dtype %d must be MOE_F32 or MOE_BF16", what, dt);
+  return MOE_OK;
+}
+
+int check_weights(const moe_weights* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights descriptor is NULL");
+  const int epc = elems_per_chunk(w->wdtype);
+  if (!epc) return fail(MOE_ERR_INVALID_ARG, "unknown weight dtype %d", w->wdtype);
+  if (w->S < 1 || w->H < 1 || w->I < 1)
+    return fail(MOE_ERR_INVALID_ARG, "S, H, I = %d, %d, %d must be >= 1", w->S, w->H, w->I);
+  if (w->S > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "S = %d above %d", w->S, kMaxE);
+  if (w->H > kMaxDim || w->I > kMaxDim)
+    return fail(MOE_ERR_UNSUPPORTED, "H = %d / I = %d above %d", w->H, w->I, kMaxDim);
+  const int m = epc < 8 ? 8 : epc;
+  if (w->H % m || w->I % m)
+    return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of %d for this dtype", w->H, w->I, m);
+  if (!w->w_gu || !w->w_d) return fail(MOE_ERR_INVALID_ARG, "w_gu / w_d is NULL");
+  if (!aligned(w->w_gu, 16) || !aligned(w->w_d, 16))
+    return fail(MOE_ERR_INVALID_ARG, "w_gu / w_d must be 16-byte aligned");
+  const bool scaled = w->wdtype == MOE_FP8_E4M3_B128 || w->wdtype == MOE_MXFP4;
+  if (scaled && (!w->s_gu || !w->s_d)) return fail(MOE_ERR_INVALID_ARG, "s_gu / s_d is NULL for a scaled dtype");
+  if (w->wdtype == MOE_FP8_E4M3_B128 && (!aligned(w->s_gu, 4) || !aligned(w->s_d, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "FP8 scales must be 4-byte aligned");
+  return MOE_OK;
+}
+
+int resolve_path(int path, int T, int k, int S) {
+  (void)T; (void)k; (void)S;
+  if (path == MOE_PATH_AUTO) return MOE_PATH_GEMV;
+  return path;
+}
+
+int check_path_mode(int path, int mode) {
+  if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
+  if (mode != MOE_MODE_A && mode != MOE_MODE_B) return fail(MOE_ERR_INVALID_ARG, "unknown mode %d", mode);
+  if (path == MOE_PATH_GEMM) return fail(MOE_ERR_UNSUPPORTED, "the GEMM path is not available in this build");
+  if (mode == MOE_MODE_B) return fail(MOE_ERR_UNSUPPORTED, "mode B needs the GEMM path");
+  return MOE_OK;
+}
+
+// workspace carving ---------------------------------------------------------------------------
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+    used += align256(bytes);
+    return p;
+  }
+};
+
+size_t ffn_ws_size(const moe_weights* w, int T, int k, int path) {
+  (void)path;
+  return 256 + align256(size_t(T) * k * w->I * sizeof(float));
+}
+
+#define MOE_TRY(expr)           \
+  do {                          \
+    int _rc = (expr);           \
+    if (_rc != MOE_OK) return _rc; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "moe-mi355x 0.1.0 (gfx950)"; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    case MOE_ERR_DEVICE: return "device-side check failed";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------------------------
+size_t moe_route_workspace_size(int T, const moe_routing* cfg, int with_router_weights) {
+  if (!cfg || T < 0 || cfg->E < 1) return 0;
+  return with_router_weights ? align256(size_t(T) * cfg->E * sizeof(float)) : 0;
+}
+
+int moe_route(const void* x, int x_dtype, int T, int H, const float* w_router, const float* logits,
+              const float* bias, const moe_routing* cfg, int32_t* topk_idx, float* topk_w,
+              float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_routing(cfg));
+  MOE_TRY(check_T(T, cfg->k));
+  if ((w_router == nullptr) == (logits == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "exactly one of w_router / logits must be given");
+  if (T > 0 && (!topk_idx || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_w is NULL");
+  if (w_router) {
+    MOE_TRY(check_act_dtype(x_dtype, "x"));
+    if (H < 4 || H % 4) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 4", H);
+    if (T > 0 && !x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+    if (!aligned(x, 16) || !aligned(w_router, 16)) return fail(MOE_ERR_INVALID_ARG, "x / w_router must be 16-byte aligned");
+    if (!logits_out && ws_bytes < moe_route_workspace_size(T, cfg, 1))
+      return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, moe_route_workspace_size(T, cfg, 1));
+    if (!logits_out && T > 0 && !ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  }
+  if (T == 0) return MOE_OK;
+  hipStream_t st = as_stream(stream);
+  const float* l = logits;
+  if (w_router) {
+    float* lo = logits_out ? logits_out : static_cast<float*>(ws);
+    hipError_t e = moe::launch_router_logits(x, x_dtype, w_router, bias, lo, T, H, cfg->E, st);
+    if (e != hipSuccess) return hip_fail(e, "router logits");
+    l = lo;
+  }
+  hipError_t e = moe::launch_topk(l, bias, (w_router == nullptr && bias) ? 1 : 0, T, cfg->E, cfg->k,
+                                  cfg->score, cfg->renorm, topk_idx, topk_w, st);
+  if (e != hipSuccess) return hip_fail(e, "top-k");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+size_t moe_permute_workspace_size(int T, const moe_routing* cfg, int S) {
+  (void)T; (void)cfg; (void)S;
+  return 256;
+}
+
+int moe_permute(const int32_t* topk_idx, const float* topk_w, int T, const moe_routing* cfg,
+                const int32_t* slot_map, int S, int32_t* counts, int32_t* slot_offsets,
+                int32_t* perm, int32_t* inv_perm, int32_t* miss_count, int32_t* miss_token,
+                int32_t* miss_expert, float* miss_weight, void* ws, size_t ws_bytes,
+                void* stream) {
+  MOE_TRY(check_routing(cfg));
+  MOE_TRY(check_T(T, cfg->k));
+  if (S < 1 || S > cfg->E) return fail(MOE_ERR_INVALID_ARG, "S = %d must be in [1, E = %d]", S, cfg->E);
+  if (!slot_map && S != cfg->E) return fail(MOE_ERR_INVALID_ARG, "without slot_map S (%d) must equal E (%d)", S, cfg->E);
+  if (!counts || !slot_offsets) return fail(MOE_ERR_INVALID_ARG, "counts / slot_offsets is NULL");
+  if (T > 0 && (!topk_idx || !perm || !inv_perm)) return fail(MOE_ERR_INVALID_ARG, "topk_idx / perm / inv_perm is NULL");
+  if (slot_map && (!miss_count || !miss_token || !miss_expert || !miss_weight || (T > 0 && !topk_w)))
+    return fail(MOE_ERR_INVALID_ARG, "a slot_map needs miss_count, miss_token, miss_expert, miss_weight and topk_w");
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < moe_permute_workspace_size(T, cfg, S))
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, moe_permute_workspace_size(T, cfg, S));
+  hipStream_t st = as_stream(stream);
+  const size_t lds = moe::permute_lds_bytes(cfg->E, S);
+  if (lds > 160 * 1024) return fail(MOE_ERR_UNSUPPORTED, "E/S too large for the permutation kernel");
+  // T = 0 still writes zero counts/offsets (one small launch)
+  hipError_t e = moe::launch_permute(topk_idx, topk_w, T, cfg->k, cfg->E, slot_map, S, counts,
+                                     slot_offsets, perm, inv_perm, miss_count, miss_token,
+                                     miss_expert, miss_weight, static_cast<uint32_t*>(ws), st);
+  if (e != hipSuccess) return hip_fail(e, "permute");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+size_t moe_expert_ffn_workspace_size(const moe_weights* w, int T, int k, int path, int mode) {
+  (void)mode;
+  if (!w || T < 0 || k < 1 || w->I < 1) return 0;
+  return ffn_ws_size(w, T, k, resolve_path(path, T, k, w->S));
+}
+
+namespace {
+
+int check_ffn_common(const moe_weights* w, int T, int k, const int32_t* slot_offsets, int path,
+                     int mode, void* ws, size_t ws_bytes) {
+  MOE_TRY(check_weights(w));
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_INVALID_ARG, "k = %d out of range", k);
+  MOE_TRY(check_T(T, k));
+  MOE_TRY(check_path_mode(path, mode));
+  if (!slot_offsets) return fail(MOE_ERR_INVALID_ARG, "slot_offsets is NULL");
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = moe_expert_ffn_workspace_size(w, T, k, path, mode);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+moe::GemvArgs gemv_args(const moe_weights* w, const void* x, int x_dtype, int T, int k,
+                        const int32_t* perm, const int32_t* off, float* y, void* ws) {
+  moe::GemvArgs g{};
+  g.wdt = w->wdtype;
+  g.xdt = x_dtype;
+  g.S = w->S;
+  g.T = T;
+  g.k = k;
+  g.H = w->H;
+  g.I = w->I;
+  const long long rows = (long long)T * k;
+  g.n_ord = int(rows < w->S ? rows : w->S);
+  g.w_gu = w->w_gu;
+  g.s_gu = w->s_gu;
+  g.w_d = w->w_d;
+  g.s_d = w->s_d;
+  g.x = x;
+  g.perm = perm;
+  g.off = off;
+  g.a = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
+  g.y = y;
+  return g;
+}
+
+}  // namespace
+
+int moe_expert_gate_up(const moe_weights* w, const void* x, int x_dtype, int T, int k,
+                       const int32_t* perm, const int32_t* slot_offsets, int path, int mode,
+                       void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_ffn_common(w, T, k, slot_offsets, path, mode, ws, ws_bytes));
+  MOE_TRY(check_act_dtype(x_dtype, "x"));
+  if (T > 0 && (!x || !perm)) return fail(MOE_ERR_INVALID_ARG, "x / perm is NULL");
+  if (!aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  if (T == 0) return MOE_OK;
+  moe::GemvArgs g = gemv_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws);
+  hipError_t e = moe::launch_gemv_gate_up(g, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "gate/up GEMV");
+  return MOE_OK;
+}
+
+int moe_expert_down(const moe_weights* w, int T, int k, const int32_t* slot_offsets, int path,
+                    int mode, float* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_ffn_common(w, T, k, slot_offsets, path, mode, ws, ws_bytes));
+  if (T > 0 && !y_perm) return fail(MOE_ERR_INVALID_ARG, "y_perm is NULL");
+  if (!aligned(y_perm, 16)) return fail(MOE_ERR_INVALID_ARG, "y_perm must be 16-byte aligned");
+  if (T == 0) return MOE_OK;
+  moe::GemvArgs g = gemv_args(w, nullptr, MOE_F32, T, k, nullptr, slot_offsets, y_perm, ws);
+  hipError_t e = moe::launch_gemv_down(g, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "down GEMV");
+  return MOE_OK;
+}
+
+int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int k,
+                   const int32_t* perm, const int32_t* slot_offsets, int path, int mode,
+                   float* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (T > 0 && !y_perm) return fail(MOE_ERR_INVALID_ARG, "y_perm is NULL");
+  MOE_TRY(moe_expert_gate_up(w, x, x_dtype, T, k, perm, slot_offsets, path, mode, ws, ws_bytes, stream));
+  return moe_expert_down(w, T, k, slot_offsets, path, mode, y_perm, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int k,
+                int H, void* out, int out_dtype, void* stream) {
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_INVALID_ARG, "k = %d out of range", k);
+  MOE_TRY(check_T(T, k));
+  if (H < 4 || H % 4) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 4", H);
+  MOE_TRY(check_act_dtype(out_dtype, "out"));
+  if (T > 0 && (!y_perm || !inv_perm || !topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "a NULL pointer");
+  if (!aligned(y_perm, 16) || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "y_perm / out must be 16-byte aligned");
+  if (T == 0) return MOE_OK;
+  hipError_t e = moe::launch_combine(y_perm, inv_perm, topk_w, T, k, H, out, out_dtype, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+namespace {
+struct LayerWs {
+  uint32_t* err;
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  int32_t* miss_count;
+  float* y;
+  void* ffn;
+  size_t used;
+};
+
+LayerWs carve_layer(void* ws, int T, const moe_routing* cfg, const moe_weights* w, int path,
+                    int with_rw) {
+  Carve c(ws);
+  LayerWs L{};
+  const size_t R = size_t(T) * cfg->k;
+  L.err = c.take<uint32_t>(256);
+  L.logits = with_rw ? c.take<float>(size_t(T) * cfg->E * 4) : nullptr;
+  L.topk_idx = c.take<int32_t>(R * 4);
+  L.topk_w = c.take<float>(R * 4);
+  L.counts = c.take<int32_t>(size_t(cfg->E) * 4);
+  L.offsets = c.take<int32_t>(size_t(w->S + 1) * 4);
+  L.perm = c.take<int32_t>(R * 4);
+  L.inv = c.take<int32_t>(R * 4);
+  L.miss_count = c.take<int32_t>(4);
+  L.y = c.take<float>(R * w->H * 4);
+  L.ffn = c.take<char>(ffn_ws_size(w, T, cfg->k, path));
+  L.used = c.used;
+  return L;
+}
+}  // namespace
+
+size_t moe_layer_workspace_size(int T, const moe_routing* cfg, const moe_weights* w, int path,
+                                int mode, int with_router_weights) {
+  (void)mode;
+  if (!cfg || !w || T < 0 || cfg->k < 1 || cfg->E < 1) return 0;
+  return carve_layer(nullptr, T, cfg, w, resolve_path(path, T, cfg->k, w->S), with_router_weights).used;
+}
+
+int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const float* logits,
+              const float* bias, const moe_routing* cfg, const int32_t* slot_map,
+              const moe_weights* w, int path, int mode, void* out, int out_dtype,
+              int32_t* topk_idx, float* topk_w, int32_t* miss_count, int32_t* miss_token,
+              int32_t* miss_expert, float* miss_weight, void* ws, size_t ws_bytes,
+              void* stream) {
+  MOE_TRY(check_routing(cfg));
+  MOE_TRY(check_T(T, cfg->k));
+  MOE_TRY(check_weights(w));
+  MOE_TRY(check_path_mode(path, mode));
+  MOE_TRY(check_act_dtype(x_dtype, "x"));
+  MOE_TRY(check_act_dtype(out_dtype, "out"));
+  if (!slot_map && w->S != cfg->E) return fail(MOE_ERR_INVALID_ARG, "without slot_map S (%d) must equal E (%d)", w->S, cfg->E);
+  if (w->S > cfg->E) return fail(MOE_ERR_INVALID_ARG, "S = %d above E = %d", w->S, cfg->E);
+  if ((w_router == nullptr) == (logits == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "exactly one of w_router / logits must be given");
+  if (slot_map && (!miss_count || !miss_token || !miss_expert || !miss_weight))
+    return fail(MOE_ERR_INVALID_ARG, "a slot_map needs miss_count, miss_token, miss_expert and miss_weight");
+  if ((topk_idx == nullptr) != (topk_w == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "give both topk_idx and topk_w or neither");
+  if (T > 0 && (!x || !out)) return fail(MOE_ERR_INVALID_ARG, "x / out is NULL");
+  if (!aligned(x, 16) || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "x / out must be 16-byte aligned");
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int rp = resolve_path(path, T, cfg->k, w->S);
+  const int with_rw = w_router != nullptr;
+  const size_t need = moe_layer_workspace_size(T, cfg, w, path, mode, with_rw);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  const size_t lds = moe::permute_lds_bytes(cfg->E, w->S);
+  if (lds > 160 * 1024) return fail(MOE_ERR_UNSUPPORTED, "E/S too large for the permutation kernel");
+  LayerWs L = carve_layer(ws, T, cfg, w, rp, with_rw);
+  int32_t* tidx = topk_idx ? topk_idx : L.topk_idx;
+  float* tw = topk_w ? topk_w : L.topk_w;
+  hipStream_t st = as_stream(stream);
+  if (T > 0) {
+    MOE_TRY(moe_route(x, x_dtype, T, w->H, w_router, logits, bias, cfg, tidx, tw, L.logits,
+                      nullptr, 0, stream));
+  }
+  hipError_t e = moe::launch_permute(tidx, tw, T, cfg->k, cfg->E, slot_map, w->S, L.counts,
+                                     L.offsets, L.perm, L.inv, miss_count ? miss_count : L.miss_count,
+                                     miss_token, miss_expert, miss_weight, L.err, st);
+  if (e != hipSuccess) return hip_fail(e, "permute");
+  if (T == 0) return MOE_OK;
+  const size_t ffn_bytes = ffn_ws_size(w, T, cfg->k, rp);
+  MOE_TRY(moe_expert_ffn(w, x, x_dtype, T, cfg->k, L.perm, L.offsets, rp, mode, L.y, L.ffn,
+                         ffn_bytes, stream));
+  return moe_combine(L.y, L.inv, tw, T, cfg->k, w->H, out, out_dtype, stream);
+}
+
+int moe_check_device_error(const void* ws, void* stream) {
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  uint32_t word = 0;
+  hipStream_t st = as_stream(stream);
+  hipError_t e = hipMemcpyAsync(&word, ws, sizeof word, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "reading the device error word");
+  if (word) return fail(MOE_ERR_DEVICE, "device error word 0x%x: out-of-range expert id or slot_map entry", word);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Permutation: expert histogram, per-slot exclusive scan and a stable scatter of the rows into
+// slot order, plus the compact miss list.  Deterministic: no global atomics, the position of
+// every row is a pure function of the routing.
+//
+// One work-group of 16 waves.  Wave w owns the contiguous row range [w*L, (w+1)*L).  Keys are
+// slots 0..S-1 plus one extra key S for non-resident rows.
+//   1. per-wave key counters in LDS (LDS atomics: counting is order-free)
+//   2. exclusive scan over keys gives slot_offsets; a running sum over waves gives each wave's
+//      base position for every key
+//   3. each wave walks its rows in chunks of 64 in order; rows of one chunk that share a key are
+//      ranked by lane order (ballot of equal keys, popcount below the lane)
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / 64;
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int k, int E,
+    const int32_t* __restrict__ slot_map, int S, int32_t* __restrict__ counts,
+    int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ miss_count, int32_t* __restrict__ miss_token,
+    int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight, uint32_t* __restrict__ err) {
+  extern __shared__ int32_t lds[];
+  const int K1 = S + 1;                     // keys: slots + the miss key
+  int32_t* cnt = lds;                       // [kPermWaves][K1] per-wave counts, then bases
+  int32_t* ecnt = cnt + kPermWaves * K1;    // [E]
+  int32_t* tot = ecnt + E;                  // [K1 + 1] key totals -> exclusive offsets
+  __shared__ int32_t wsum[kPermWaves];
+  __shared__ uint32_t bad;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int R = T * k;
+  const int L = (R + kPermWaves - 1) / kPermWaves;
+  const int r0 = wid * L, r1 = min(R, r0 + L);
+
+  for (int i = tid; i < kPermWaves * K1; i += kPermThreads) cnt[i] = 0;
+  for (int i = tid; i < E; i += kPermThreads) ecnt[i] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+
+  // key of a row: slot, S for a miss, -1 for an invalid row
+  auto key_of = [&](int r, int& e) -> int {
+    e = topk_idx[r];
+    if (e < 0 || e >= E) return -1;
+    int s = slot_map ? slot_map[e] : e;
+    if (s < -1 || s >= S) return -1;
+    return s < 0 ? S : s;
+  };
+
+  // 1. counts
+  for (int r = r0 + lane; r < r1; r += 64) {
+    int e;
+    const int key = key_of(r, e);
+    if (key < 0) {
+      bad = 1;
+      continue;
+    }
+    atomicAdd(&cnt[wid * K1 + key], 1);
+    atomicAdd(&ecnt[e], 1);
+  }
+  __syncthreads();
+
+  // 2a. key totals
+  for (int key = tid; key < K1; key += kPermThreads) {
+    int s = 0;
+    for (int w = 0; w < kPermWaves; ++w) s += cnt[w * K1 + key];
+    tot[key] = s;
+  }
+  __syncthreads();
+  // 2b. exclusive scan of the S slot totals (the miss key scans separately from 0):
+  //     thread-sequential chunks, then a scan of the chunk sums.
+  {
+    const int per = (S + kPermThreads - 1) / kPermThreads;
+    const int a = tid * per, b = min(S, a + per);
+    int local = 0;
+    for (int i = a; i < b; ++i) local += tot[i];
+    // inclusive wave scan of `local`
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wid; ++w) wbase += wsum[w];
+    int run = wbase + incl - local;
+    __syncthreads();
+    for (int i = a; i < b; ++i) {
+      const int c = tot[i];
+      tot[i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int n_res = 0;
+    for (int w = 0; w < kPermWaves; ++w) n_res += wsum[w];
+    tot[S + 1] = n_res;
+  }
+  __syncthreads();
+  // 2c. per-wave bases: base[w][key] = offset[key] + sum_{w' < w} cnt[w'][key]
+  for (int key = tid; key < K1; key += kPermThreads) {
+    int run = (key == S) ? 0 : tot[key];
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = cnt[w * K1 + key];
+      cnt[w * K1 + key] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+
+  // 3. stable scatter
+  for (int c0 = r0; c0 < r1; c0 += 64) {
+    const int r = c0 + lane;
+    int e = 0, key = -1;
+    if (r < r1) key = key_of(r, e);
+    unsigned long long todo = __ballot(key >= 0);
+    int pos = -1;
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int lkey = __shfl(key, leader);
+      const unsigned long long m = __ballot(key == lkey);
+      const int b = cnt[wid * K1 + lkey];
+      if (key == lkey) pos = b + __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == leader) cnt[wid * K1 + lkey] = b + __popcll(m);
+      todo &= ~m;
+    }
+    if (r < r1) {
+      if (key < 0) {
+        inv_perm[r] = -1;
+      } else if (key < S) {
+        perm[pos] = r;
+        inv_perm[r] = pos;
+      } else {
+        inv_perm[r] = -1;
+        miss_token[pos] = r / k;
+        miss_expert[pos] = e;
+        miss_weight[pos] = topk_w[r];
+      }
+    }
+  }
+
+  // outputs of the scan and histogram
+  for (int i = tid; i < E; i += kPermThreads) counts[i] = ecnt[i];
+  for (int i = tid; i < S; i += kPermThreads) slot_offsets[i] = tot[i];
+  if (tid == 0) {
+    slot_offsets[S] = tot[S + 1];
+    if (miss_count) miss_count[0] = tot[S];
+    err[0] = bad ? 1u : 0u;
+  }
+}
+
+size_t permute_lds_bytes(int E, int S) {
+  return sizeof(int32_t) * (size_t(kPermWaves) * (S + 1) + E + (S + 2));
+}
+
+hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
+                          const int32_t* slot_map, int S, int32_t* counts, int32_t* slot_offsets,
+                          int32_t* perm, int32_t* inv_perm, int32_t* miss_count,
+                          int32_t* miss_token, int32_t* miss_expert, float* miss_weight,
+                          uint32_t* err, hipStream_t st) {
+  const size_t lds = permute_lds_bytes(E, S);
+  permute_kernel<<<1, kPermThreads, lds, st>>>(topk_idx, topk_w, T, k, E, slot_map, S, counts,
+                                               slot_offsets, perm, inv_perm, miss_count,
+                                               miss_token, miss_expert, miss_weight, err);
+  return hipGetLastError();
+}
+
+}  // namespace moe

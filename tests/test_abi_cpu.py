@@ -1,0 +1,154 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/moe.h declares, and
+rejects malformed arguments on the host (validation precedes every HIP call, so none of these
+calls touches a device)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import routed_expert_ffn_05_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe_hip.so is not built (run python -m routed_expert_ffn_05_amd.build)")
+    return moe.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = _declared()
+    assert len(names) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(moe.exported_symbols()) == names       # the binding covers exactly the header
+
+
+def test_version_and_status_strings(L):
+    assert "gfx950" in moe.version()
+    assert moe.status_string(moe.MOE_ERR_WORKSPACE) == "workspace too small"
+    assert moe.status_string(12345) == "unknown status"
+
+
+def _expect(status, fn, *args, **kw):
+    with pytest.raises(moe.MoeError) as ei:
+        fn(*args, **kw)
+    assert ei.value.status == status, str(ei.value)
+    return str(ei.value)
+
+
+FAKE = 1 << 20          # a non-NULL, 256-byte aligned address never dereferenced by validation
+
+
+def test_route_validation(L):
+    cfg = moe.routing(8, 2, "softmax")
+    # both / neither of w_router and logits
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, FAKE, moe.MOE_F32, 4, 64, FAKE, FAKE, None, cfg, FAKE, FAKE,
+            None, FAKE, 1 << 20, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, FAKE, moe.MOE_F32, 4, 64, None, None, None, cfg, FAKE, FAKE,
+            None, FAKE, 1 << 20, 0)
+    # k > E, k = 0, E too large, bad score
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, None, 0, 4, 64, None, FAKE, None, moe.routing(8, 9, 0),
+            FAKE, FAKE, None, None, 0, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, None, 0, 4, 64, None, FAKE, None, moe.routing(8, 0, 0),
+            FAKE, FAKE, None, None, 0, 0)
+    _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_route, None, 0, 4, 64, None, FAKE, None, moe.routing(4096, 8, 0),
+            FAKE, FAKE, None, None, 0, 0)
+    _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_route, None, 0, 4, 64, None, FAKE, None, moe.routing(128, 65, 0),
+            FAKE, FAKE, None, None, 0, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, None, 0, 4, 64, None, FAKE, None, moe.routing(8, 2, 7),
+            FAKE, FAKE, None, None, 0, 0)
+    # negative T; missing outputs; misaligned x; short workspace
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, None, 0, -1, 64, None, FAKE, None, cfg, FAKE, FAKE, None,
+            None, 0, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, None, 0, 4, 64, None, FAKE, None, cfg, None, FAKE, None,
+            None, 0, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, FAKE + 4, moe.MOE_F32, 4, 64, FAKE, None, None, cfg, FAKE,
+            FAKE, None, FAKE, 1 << 20, 0)
+    msg = _expect(moe.MOE_ERR_WORKSPACE, moe.moe_route, FAKE, moe.MOE_F32, 4, 64, FAKE, None, None, cfg, FAKE,
+                  FAKE, None, FAKE, 16, 0)
+    assert "need" in msg
+    assert moe.moe_route_workspace_size(4, cfg, 1) >= 4 * 8 * 4
+
+
+def test_permute_validation(L):
+    cfg = moe.routing(16, 2, "sigmoid")
+    args = dict(topk_idx=FAKE, topk_w=FAKE, T=4, cfg=cfg, slot_map=None, S=16, counts=FAKE, slot_offsets=FAKE,
+                perm=FAKE, inv_perm=FAKE, miss_count=None, miss_token=None, miss_expert=None, miss_weight=None,
+                ws=FAKE, ws_bytes=256, stream=0)
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return moe.moe_permute(*a.values())
+    _expect(moe.MOE_ERR_INVALID_ARG, call, S=8)                              # S != E without a map
+    _expect(moe.MOE_ERR_INVALID_ARG, call, slot_map=FAKE, S=8)                # map without miss buffers
+    _expect(moe.MOE_ERR_INVALID_ARG, call, S=17)
+    _expect(moe.MOE_ERR_INVALID_ARG, call, ws=FAKE + 64)                      # misaligned workspace
+    _expect(moe.MOE_ERR_WORKSPACE, call, ws_bytes=8)
+    _expect(moe.MOE_ERR_INVALID_ARG, call, perm=None)
+
+
+def test_expert_ffn_validation(L):
+    def w(dt, S=8, H=256, I=128, sc=True):
+        return moe.weights(dt, S, H, I, FAKE, FAKE if sc else None, FAKE, FAKE if sc else None)
+    big = 1 << 30
+    ok = dict(w=w("bf16"), x=FAKE, x_dtype=moe.MOE_BF16, T=4, k=2, perm=FAKE, slot_offsets=FAKE,
+              path=moe.MOE_PATH_GEMV, mode=moe.MOE_MODE_A, y_perm=FAKE, ws=FAKE, ws_bytes=big, stream=0)
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return moe.moe_expert_ffn(*a.values())
+    _expect(moe.MOE_ERR_INVALID_ARG, call, w=w(9))                            # unknown dtype
+    _expect(moe.MOE_ERR_INVALID_ARG, call, w=w("fp8", sc=False))              # scaled dtype without scales
+    _expect(moe.MOE_ERR_UNSUPPORTED, call, w=w("mxfp4", H=272))               # K % 32 for MXFP4
+    _expect(moe.MOE_ERR_UNSUPPORTED, call, w=w("fp8", I=136))                 # K % 16 for FP8
+    _expect(moe.MOE_ERR_UNSUPPORTED, call, w=w("bf16", H=16384))
+    _expect(moe.MOE_ERR_INVALID_ARG, call, x_dtype=moe.MOE_FP8_E4M3_B128)
+    _expect(moe.MOE_ERR_INVALID_ARG, call, path=7)
+    _expect(moe.MOE_ERR_INVALID_ARG, call, mode=5)
+    _expect(moe.MOE_ERR_INVALID_ARG, call, x=FAKE + 8)
+    _expect(moe.MOE_ERR_WORKSPACE, call, ws_bytes=1024)
+    _expect(moe.MOE_ERR_INVALID_ARG, call, slot_offsets=None)
+    n = moe.moe_expert_ffn_workspace_size(w("bf16"), 4, 2, moe.MOE_PATH_GEMV, moe.MOE_MODE_A)
+    assert n >= 4 * 2 * 128 * 4
+
+
+def test_combine_and_layer_validation(L):
+    _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_combine, FAKE, FAKE, FAKE, 4, 2, 30, FAKE, moe.MOE_F32, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_combine, FAKE, FAKE, FAKE, 4, 2, 64, FAKE, 3, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_combine, FAKE, None, FAKE, 4, 2, 64, FAKE, moe.MOE_F32, 0)
+    cfg = moe.routing(16, 2, "sigmoid")
+    w = moe.weights("bf16", 16, 256, 128, FAKE, None, FAKE, None)
+    big = moe.moe_layer_workspace_size(4, cfg, w, moe.MOE_PATH_AUTO, moe.MOE_MODE_A, 0)
+    assert big > 4 * 2 * 256 * 4
+    base = [FAKE, moe.MOE_BF16, 4, None, FAKE, None, cfg, None, w, moe.MOE_PATH_AUTO, moe.MOE_MODE_A, FAKE,
+            moe.MOE_BF16, None, None, None, None, None, None, FAKE, big, 0]
+    bad = list(base)
+    bad[7] = FAKE                                                          # slot map without miss buffers
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_layer, *bad)
+    bad = list(base)
+    bad[-2] = 100
+    _expect(moe.MOE_ERR_WORKSPACE, moe.moe_layer, *bad)
+    bad = list(base)
+    bad[13] = FAKE                                                         # topk_idx without topk_w
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_layer, *bad)
+    bad = list(base)
+    bad[8] = moe.weights("bf16", 8, 256, 128, FAKE, None, FAKE, None)      # S != E without a map
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_layer, *bad)
+
+
+def test_last_error_is_per_call(L):
+    _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_combine, FAKE, FAKE, FAKE, 4, 2, 30, FAKE, moe.MOE_F32, 0)
+    assert "H = 30" in moe.lib().moe_last_error().decode()

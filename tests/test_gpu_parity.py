@@ -1,0 +1,142 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on seeded inputs.
+
+Shrunken cases finish in the oracle in seconds yet span several work-group tiles with ragged
+tails (T, I and H not multiples of the tile sizes, uneven and empty slot groups); every stage is
+also checked on its own with the oracle's results as its inputs."""
+import sys
+
+import numpy as np
+import pytest
+
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": gen.config("tiny"),
+    "f32_sigmoid_norenorm": gen.config("tiny", T=21, score="sigmoid", renorm=False, I=136),
+    "bf16_ragged": gen.config("decode_bf16", T=37, H=512, E=24, I=136, k=4),
+    "fp8_ragged": gen.config("decode_fp8", T=29, H=384, E=20, I=272, k=3),
+    "fp8_zipf": gen.config("prefill_fp8_zipf", T=300, H=256, E=32, I=128, k=8),
+    "mxfp4_compact": gen.config("compact_mxfp4", T=53, H=512, E=40, I=160, k=6, resident=13),
+    "mxfp4_compact_t1": gen.config("compact_mxfp4", T=1, H=256, E=16, I=128, k=4, resident=5),
+}
+
+
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _banner(name, cfg):
+    print(f"[gpu-parity] case={name} T={cfg.T} H={cfg.H} E={cfg.E} I={cfg.I} k={cfg.k} "
+          f"w={cfg.wdtype} S={cfg.S}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", params=list(SMALL))
+def small_case(request):
+    _gpu()
+    from gpu_cases import GpuCase, run_oracle
+    cfg = SMALL[request.param]
+    inp = gen.make_inputs(cfg, bias=(request.param == "bf16_ragged"))
+    return request.param, inp, GpuCase(inp), run_oracle(inp)
+
+
+def test_route_stage(small_case):
+    from gpu_cases import check_routing
+    name, inp, g, ref = small_case
+    _banner(name + "/route", inp.cfg)
+    idx, w, lo = g.route()
+    check_routing(idx, w, ref)
+    if lo is not None:
+        np.testing.assert_allclose(lo, ref["logits"] if inp.bias is None else ref["logits"] + inp.bias,
+                                   rtol=1e-4, atol=1e-5 * np.abs(ref["logits"]).max())
+
+
+def test_permute_stage(small_case):
+    from gpu_cases import check_permute
+    name, inp, g, ref = small_case
+    _banner(name + "/permute", inp.cfg)
+    res = g.permute(ref["topk_idx"], ref["topk_w"])
+    check_permute(res, ref)
+
+
+def test_expert_ffn_stage(small_case):
+    import routed_expert_ffn_05_amd as moe
+    from gpu_cases import assert_fp_close
+    name, inp, g, ref = small_case
+    _banner(name + "/expert_ffn", inp.cfg)
+    y = g.expert_ffn(ref["perm"], ref["slot_offsets"], path=moe.MOE_PATH_GEMV)
+    assert_fp_close(y, ref["y_perm"], f"{name} y_perm (GEMV)")
+
+
+def test_combine_stage(small_case):
+    from gpu_cases import assert_fp_close
+    name, inp, g, ref = small_case
+    _banner(name + "/combine", inp.cfg)
+    out = g.combine(ref["y_perm"].astype(np.float32), ref["inv_perm"], ref["topk_w"].astype(np.float32))
+    assert_fp_close(out, ref["out"], f"{name} combine")
+
+
+def test_layer(small_case):
+    from gpu_cases import assert_fp_close, check_misses, check_routing
+    name, inp, g, ref = small_case
+    _banner(name + "/layer", inp.cfg)
+    res = g.layer()
+    flipped = check_routing(res["topk_idx"], res["topk_w"], ref)
+    keep = np.array([t not in flipped for t in range(inp.cfg.T)], bool)
+    assert_fp_close(res["out"][keep], ref["out"][keep], f"{name} layer out")
+    if not flipped:
+        check_misses(res, ref)
+
+
+def test_layer_is_deterministic(small_case):
+    name, inp, g, ref = small_case
+    _banner(name + "/determinism", inp.cfg)
+    a = g.layer()
+    b = g.layer()
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["topk_idx"], b["topk_idx"])
+
+
+def test_empty_batch():
+    _gpu()
+    from gpu_cases import GpuCase
+    cfg = gen.config("decode_bf16", T=0, H=256, E=16, I=128, k=4)
+    inp = gen.make_inputs(cfg)
+    g = GpuCase(inp)
+    res = g.layer()
+    assert res["out"].shape == (0, cfg.H)
+    p = g.permute(np.zeros((0, cfg.k), np.int32), np.zeros((0, cfg.k), np.float32))
+    assert np.all(p["counts"] == 0) and np.all(p["slot_offsets"] == 0)
+
+
+def test_all_rows_missing():
+    # compact map with no routed expert resident: zero output rows, every row in the miss list
+    _gpu()
+    from gpu_cases import GpuCase, check_misses, run_oracle
+    cfg = gen.config("compact_mxfp4", T=6, H=256, E=16, I=128, k=2, resident=3)
+    inp = gen.make_inputs(cfg)
+    lg = np.zeros((cfg.T, cfg.E), np.float32)
+    resident = np.nonzero(inp.slot_map >= 0)[0]
+    lg[:, resident] = -10.0
+    inp.logits = lg
+    g = GpuCase(inp)
+    ref = run_oracle(inp)
+    res = g.layer()
+    assert np.all(res["out"] == 0)
+    check_misses(res, ref)
+    assert res["miss_count"] == cfg.T * cfg.k
+
+
+def test_out_of_range_expert_sets_device_error():
+    _gpu()
+    import routed_expert_ffn_05_amd as moe
+    from gpu_cases import GpuCase
+    cfg = gen.config("decode_bf16", T=4, H=256, E=16, I=128, k=2)
+    g = GpuCase(gen.make_inputs(cfg))
+    idx = np.array([[0, 1], [2, 99], [3, 4], [5, -1]], np.int32)
+    with pytest.raises(moe.MoeError) as ei:
+        g.permute(idx, np.full((4, 2), 0.5, np.float32))
+    assert ei.value.status == moe.MOE_ERR_DEVICE

@@ -1,0 +1,396 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_bf16]
+
+A step is one pass of the whole layer -- router logits and top-k, permutation, expert gate/up
+and down projections, combine -- over one batch of synthetic tokens, with every input resident in
+HBM before the timed region starts.  Batches rotate over ``--rotate`` pre-generated activation
+(or logit) sets so that consecutive steps route to different experts.  Prints ONE JSON line.
+
+The default workload is the bf16 decode layer: T=4 tokens, hidden 4096, 384 experts, expert
+intermediate 1024, top-8 sigmoid routing with renormalised gates.
+
+The ``roofline`` object describes the dominant kernel (the expert gate/up projection, 2/3 of the
+layer's bytes): algorithmic bytes per launch over its average duration, measured with HIP events
+recorded on the launch stream around every timed launch.  ``cpu_baseline`` times the CPU oracle
+on a bounded sample of the same workload.
+
+Profiling helpers (no GPU work of their own):
+    python bench.py --copy-probe-mib 512 ...   also launches one plain device copy of known size
+    python bench.py --summarize-kernels DIR --out FILE   rocprofv3 --stats CSV -> summary text
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --out FILE   PMC CSVs -> traffic summary
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0}
+PROFILES = os.path.join(ROOT, "profiles")
+GATE_UP_SOURCES = ["routed_expert_ffn_05_amd/csrc/gemv.hip", "routed_expert_ffn_05_amd/csrc/common.h"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------------------------
+
+def _csvs(d, pattern):
+    return sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+
+
+def summarize_kernels(d, out, command):
+    rows = []
+    for f in _csvs(d, "*kernel_stats.csv"):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# rocprofv3 kernel statistics", "", f"command: `{command}`", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = name.split("(")[0][:90]
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _pmc_per_kernel(d, counter):
+    """{kernel short name: [per-dispatch counter values]} from rocprofv3 counter_collection CSVs."""
+    res = {}
+    for f in _csvs(d, "*counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r.get("Kernel_Name", "").split("(")[0]
+                res.setdefault(name, []).append(float(r["Counter_Value"]))
+    return res
+
+
+def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kernel_key, copy_bytes,
+                  bytes_per_launch):
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(dct, key):
+        ks = [k for k in dct if key in k]
+        if not ks:
+            raise SystemExit(f"no kernel matching {key!r} in {sorted(dct)}")
+        return dct[ks[0]]
+
+    # the copy probe: the largest-fetch elementwise copy kernel
+    copy_keys = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    copy_f = max((max(fetch[k]) for k in copy_keys), default=None)
+    copy_wk = [k for k in write if "copy" in k.lower() or "elementwise" in k.lower()]
+    copy_w = max((max(write[k]) for k in copy_wk), default=None)
+    f_factor = copy_bytes / (copy_f * 1024.0) if copy_f else None
+    w_factor = copy_bytes / (copy_w * 1024.0) if copy_w else None
+    kf = pick(fetch, kernel_key)
+    kw = pick(write, kernel_key)
+    fetch_b = sum(kf) / len(kf) * 1024.0 * (f_factor or 1.0)
+    write_b = sum(kw) / len(kw) * 1024.0 * (w_factor or 1.0)
+    lines = ["# HBM traffic of the gate/up GEMV (rocprofv3 PMC)", "",
+             f"fetch command: `{command_fetch}`", f"write command: `{command_write}`", "",
+             f"kernel: `{kernel_key}`, dispatches: {len(kf)} (FETCH_SIZE), {len(kw)} (WRITE_SIZE)",
+             f"copy probe: {copy_bytes} bytes; FETCH_SIZE {copy_f} KiB -> factor {f_factor}; "
+             f"WRITE_SIZE {copy_w} KiB -> factor {w_factor}",
+             f"mean FETCH_SIZE per dispatch (scaled): {fetch_b:.0f} bytes",
+             f"mean WRITE_SIZE per dispatch (scaled): {write_b:.0f} bytes",
+             f"algorithmic bytes per launch (same run): {bytes_per_launch:.0f}",
+             "",
+             f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+             f"source_hash: {source_hash(GATE_UP_SOURCES)}"]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def recorded_traffic(workload_key):
+    """(traffic bytes per launch, ok) from the committed PMC summary, None if the kernel changed."""
+    p = os.path.join(PROFILES, f"gate_up_gemv_{workload_key}_pmc.md")
+    if not os.path.exists(p):
+        return None
+    vals = {}
+    for line in open(p):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_hash"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash(GATE_UP_SOURCES):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------------------------
+# the benchmark
+# ---------------------------------------------------------------------------------------------
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import routed_expert_ffn_05_amd as moe
+    from routed_expert_ffn_05_amd import device as D
+    from synth import gen
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    moe.lib()  # fail loudly without the HIP library
+    torch.cuda.set_device(0)
+    over = {}
+    if args.T is not None:
+        over["T"] = args.T
+    cfg = gen.config(args.config, **over)
+    T, H, I, E, k, S = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.S
+    t0 = time.time()
+    slot_map, slot_expert = gen.make_slot_map(cfg)
+    host_w = gen.stack_weights(cfg, slot_expert)
+    log(f"generated {cfg.name} weights ({S} slots) in {time.time() - t0:.1f}s")
+    w = D.upload_weights(cfg.wdtype, H, I, host_w)
+    if not args.cpu_baseline:
+        host_w = None
+    rot = []
+    for r in range(args.rotate):
+        rc = cfg.replace(seed=cfg.seed * 1000 + 17 + r) if r else cfg
+        x = gen.make_x(rc)
+        lg = gen.make_logits(rc) if cfg.router != "weights" else None
+        rot.append((x, lg))
+    d_x = [D.to_device(x) for x, _ in rot]
+    d_lg = [D.to_device(lg) if lg is not None else None for _, lg in rot]
+    d_wr = D.to_device(gen.make_router_weights(cfg)) if cfg.router == "weights" else None
+    d_sm = D.to_device(slot_map)
+    xdt = moe.MOE_BF16 if cfg.xdtype == "bf16" else moe.MOE_F32
+    odt = moe.MOE_BF16 if cfg.out_dtype == "bf16" else moe.MOE_F32
+    rcfg = moe.routing(E, k, cfg.score, cfg.renorm)
+    desc = w.desc
+    path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[args.path]
+    mode = {"A": moe.MOE_MODE_A, "B": moe.MOE_MODE_B}[args.mode]
+    R = T * k
+    dev = "cuda"
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    logits_buf = torch.empty((T, E), dtype=torch.float32, device=dev) if d_wr is not None else None
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    off = torch.empty(S + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(R, dtype=torch.int32, device=dev)
+    inv = torch.empty(R, dtype=torch.int32, device=dev)
+    mc = torch.zeros(1, dtype=torch.int32, device=dev)
+    mt = torch.empty(R, dtype=torch.int32, device=dev)
+    me = torch.empty(R, dtype=torch.int32, device=dev)
+    mw = torch.empty(R, dtype=torch.float32, device=dev)
+    y = torch.empty((R, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.int16 if odt == moe.MOE_BF16 else torch.float32, device=dev)
+    pws = D.workspace(moe.moe_permute_workspace_size(T, rcfg, S))
+    fbytes = moe.moe_expert_ffn_workspace_size(desc, T, k, path, mode)
+    fws = D.workspace(fbytes)
+    compact = d_sm is not None
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(i, ev=None):
+        r = i % len(rot)
+        moe.moe_route(d_x[r], xdt, T, H, d_wr, d_lg[r], None, rcfg, topk_idx, topk_w, logits_buf, None, 0, sp)
+        moe.moe_permute(topk_idx, topk_w, T, rcfg, d_sm, S, counts, off, perm, inv, mc if compact else None,
+                        mt if compact else None, me if compact else None, mw if compact else None, pws,
+                        pws.numel(), sp)
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_expert_gate_up(desc, d_x[r], xdt, T, k, perm, off, path, mode, fws, fbytes, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.moe_expert_down(desc, T, k, off, path, mode, y, fws, fbytes, sp)
+        moe.moe_combine(y, inv, topk_w, T, k, H, out, odt, sp)
+
+    # per-rotation routing statistics (outside the timed region)
+    per_rot = []
+    for r in range(len(rot)):
+        step(r)
+        torch.cuda.synchronize()
+        cnt = counts.cpu().numpy()
+        if slot_map is not None:
+            res = slot_map >= 0
+            touched = int(((cnt > 0) & res).sum())
+            n_res = int(cnt[res].sum())
+        else:
+            touched = int((cnt > 0).sum())
+            n_res = int(cnt.sum())
+        per_rot.append((touched, n_res))
+    slot_bytes_gu = (w.w_gu.numel() * w.w_gu.element_size() + (0 if w.s_gu is None else w.s_gu.numel() * w.s_gu.element_size())) // S
+    slot_bytes_d = (w.w_d.numel() * w.w_d.element_size() + (0 if w.s_d is None else w.s_d.numel() * w.s_d.element_size())) // S
+    xb = 2 if cfg.xdtype == "bf16" else 4
+
+    def gate_up_bytes(r):
+        touched, n_res = per_rot[r]
+        return touched * slot_bytes_gu + T * H * xb + n_res * I * 4
+
+    def layer_bytes(r):
+        touched, n_res = per_rot[r]
+        b = touched * (slot_bytes_gu + slot_bytes_d) + T * H * xb + T * H * (2 if odt == moe.MOE_BF16 else 4)
+        b += (E * H * 4) if d_wr is not None else T * E * 4
+        return b
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    gu_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = T * args.steps / (total_ms / 1e3)
+    gu_bytes = [gate_up_bytes(i % len(rot)) for i in range(args.steps)]
+    achieved = sum(gu_bytes) / (sum(gu_ms) / 1e3) / 1e9
+    layer_gbs = sum(layer_bytes(i % len(rot)) for i in range(args.steps)) / (total_ms / 1e3) / 1e9
+    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step), "
+        f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s")
+
+    if args.copy_probe_mib:
+        nb = args.copy_probe_mib << 20
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: {nb} bytes")
+
+    key = f"{cfg.name}_T{T}"
+    traffic = recorded_traffic(key)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "gemv_gate_up_kernel", "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
+                "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2)}
+
+    cpu = None
+    if args.cpu_baseline:
+        cpu = cpu_baseline(cfg, rot, host_w, slot_map, args.cpu_seconds)
+
+    rec = {
+        "metric": "MoE layer tokens/s",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations",
+                  "mxfp4": "mxfp4 weights, bf16 activations"}[cfg.wdtype],
+        "data": "synthetic (seeded; random-init weights of the layer's shape)",
+        "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} I={I} k={k} S={S} "
+                               f"{cfg.score}-renorm weights={cfg.wdtype}",
+                   "tokens_per_step": T, "rotations": len(rot), "path": args.path, "mode": args.mode,
+                   "layer_algorithmic_GBs": round(layer_gbs, 1),
+                   "touched_slots_per_step": round(float(np.mean([p[0] for p in per_rot])), 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(cfg, rot, host_w, slot_map, budget_s):
+    """Time the CPU oracle (fp64 numpy) on whole batches of the same workload until ~budget_s."""
+    from oracle import moe_oracle as O
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    wr = gen.make_router_weights(cfg) if cfg.router == "weights" else None
+    n_tok, spent, batches = 0, 0.0, 0
+    for x, lg in rot:
+        t0 = time.perf_counter()
+        O.layer(x, cfg.xdtype, host_w, cfg.wdtype, cfg.H, cfg.I, cfg.E, cfg.k, cfg.score, cfg.renorm,
+                w_router=wr, logits=lg, slot_map=slot_map, S=cfg.S)
+        spent += time.perf_counter() - t0
+        n_tok += cfg.T
+        batches += 1
+        log(f"cpu oracle batch {batches}: {spent:.1f}s")
+        if spent >= budget_s:
+            break
+    return {"value": round(n_tok / spent, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{batches} batch(es) x {cfg.T} tokens of the same workload through the whole fp64 "
+                      f"oracle layer (routing, permutation, per-slot dequantisation, FFN, combine), "
+                      f"{spent:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode_bf16")
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--mode", default="A", choices=["A", "B"])
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--summarize-kernels", default=None)
+    ap.add_argument("--summarize-pmc", nargs=2, default=None)
+    ap.add_argument("--pmc-kernel", default="gemv_gate_up_kernel")
+    ap.add_argument("--pmc-copy-bytes", type=int, default=512 << 20)
+    ap.add_argument("--pmc-bytes-per-launch", type=float, default=0.0)
+    ap.add_argument("--command", nargs="*", default=[])
+    ap.add_argument("--out", default=None)
+    a = ap.parse_args(argv)
+    if a.summarize_kernels:
+        summarize_kernels(a.summarize_kernels, a.out, " ".join(a.command))
+        return 0
+    if a.summarize_pmc:
+        cmds = " ".join(a.command).split(" ;; ")
+        summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], a.out, cmds[0], cmds[-1], a.pmc_kernel,
+                      a.pmc_copy_bytes, a.pmc_bytes_per_launch)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}, "
+              f"WORLD_SIZE {world}). Run with --gpus 1.", file=sys.stderr)
+        return 2
+    run(a)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

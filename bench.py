@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0}
 PROFILES = os.path.join(ROOT, "profiles")
-GATE_UP_SOURCES = ["routed_expert_ffn_05_amd/csrc/gemv.hip", "routed_expert_ffn_05_amd/csrc/common.h"]
+GATE_UP_SOURCES = ["routed_expert_ffn_05_amd/csrc/gemv_impl.h", "routed_expert_ffn_05_amd/csrc/common.h"]
 
 
 def log(*a):
@@ -106,9 +106,9 @@ def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kerne
         return dct[ks[0]]
 
     # the copy probe: the largest-fetch elementwise copy kernel
-    copy_keys = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    copy_keys = [k for k in fetch if "neg" in k.lower()]
     copy_f = max((max(fetch[k]) for k in copy_keys), default=None)
-    copy_wk = [k for k in write if "copy" in k.lower() or "elementwise" in k.lower()]
+    copy_wk = [k for k in write if "neg" in k.lower()]
     copy_w = max((max(write[k]) for k in copy_wk), default=None)
     f_factor = copy_bytes / (copy_f * 1024.0) if copy_f else None
     w_factor = copy_bytes / (copy_w * 1024.0) if copy_w else None
@@ -198,7 +198,6 @@ def run(args):
     dev = "cuda"
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    logits_buf = torch.empty((T, E), dtype=torch.float32, device=dev) if d_wr is not None else None
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     off = torch.empty(S + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(R, dtype=torch.int32, device=dev)
@@ -209,7 +208,8 @@ def run(args):
     mw = torch.empty(R, dtype=torch.float32, device=dev)
     y = torch.empty((R, H), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.int16 if odt == moe.MOE_BF16 else torch.float32, device=dev)
-    pws = D.workspace(moe.moe_permute_workspace_size(T, rcfg, S))
+    rp_bytes = moe.moe_route_permute_workspace_size(T, rcfg, S, d_wr is not None)
+    pws = D.workspace(rp_bytes)
     fbytes = moe.moe_expert_ffn_workspace_size(desc, T, k, path, mode)
     fws = D.workspace(fbytes)
     compact = d_sm is not None
@@ -218,10 +218,9 @@ def run(args):
 
     def step(i, ev=None):
         r = i % len(rot)
-        moe.moe_route(d_x[r], xdt, T, H, d_wr, d_lg[r], None, rcfg, topk_idx, topk_w, logits_buf, None, 0, sp)
-        moe.moe_permute(topk_idx, topk_w, T, rcfg, d_sm, S, counts, off, perm, inv, mc if compact else None,
-                        mt if compact else None, me if compact else None, mw if compact else None, pws,
-                        pws.numel(), sp)
+        moe.moe_route_permute(d_x[r], xdt, T, H, d_wr, d_lg[r], None, rcfg, d_sm, S, topk_idx, topk_w, counts,
+                              off, perm, inv, mc if compact else None, mt if compact else None,
+                              me if compact else None, mw if compact else None, pws, rp_bytes, sp)
         if ev is not None:
             ev[0].record(stream)
         moe.moe_expert_gate_up(desc, d_x[r], xdt, T, k, perm, off, path, mode, fws, fbytes, sp)
@@ -281,21 +280,32 @@ def run(args):
     log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step), "
         f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s")
 
+    # the staged step is moe_layer's own sequence: check one rotation bit for bit
+    lay = D.Layer(T=T, H=H, I=I, E=E, k=k, score=cfg.score, renorm=cfg.renorm, xdtype=cfg.xdtype,
+                  out_dtype=cfg.out_dtype, weights=w, w_router=d_wr, slot_map=d_sm, path=path, mode=mode)
+    step(0)
+    lay(d_x[0], d_lg[0])
+    torch.cuda.synchronize()
+    if not torch.equal(lay.out, out):
+        raise SystemExit("bench: staged step and moe_layer disagree")
+    del lay
+
     if args.copy_probe_mib:
+        # a plain elementwise kernel that reads nb bytes and writes nb bytes (scales the counters)
         nb = args.copy_probe_mib << 20
-        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        a = torch.empty(nb // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        a.fill_(1)
+        a.fill_(1.0)
         torch.cuda.synchronize()
-        b.copy_(a)
+        torch.neg(a, out=b)
         torch.cuda.synchronize()
-        log(f"copy probe: {nb} bytes")
+        log(f"copy probe: {nb} bytes read and written")
 
     key = f"{cfg.name}_T{T}"
     traffic = recorded_traffic(key)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "gemv_gate_up_kernel", "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
+                "kernel": "moe::gemv::gate_up_kernel", "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
                 "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2)}
 
     cpu = None
@@ -338,14 +348,16 @@ def cpu_baseline(cfg, rot, host_w, slot_map, budget_s):
         cores = 1
     wr = gen.make_router_weights(cfg) if cfg.router == "weights" else None
     n_tok, spent, batches = 0, 0.0, 0
-    for x, lg in rot:
+    for i in range(1000):
+        x, lg = rot[i % len(rot)]
         t0 = time.perf_counter()
         O.layer(x, cfg.xdtype, host_w, cfg.wdtype, cfg.H, cfg.I, cfg.E, cfg.k, cfg.score, cfg.renorm,
                 w_router=wr, logits=lg, slot_map=slot_map, S=cfg.S)
         spent += time.perf_counter() - t0
         n_tok += cfg.T
         batches += 1
-        log(f"cpu oracle batch {batches}: {spent:.1f}s")
+        if batches % 10 == 0:
+            log(f"cpu oracle batch {batches}: {spent:.1f}s")
         if spent >= budget_s:
             break
     return {"value": round(n_tok / spent, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
@@ -369,7 +381,7 @@ def main(argv=None):
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--summarize-kernels", default=None)
     ap.add_argument("--summarize-pmc", nargs=2, default=None)
-    ap.add_argument("--pmc-kernel", default="gemv_gate_up_kernel")
+    ap.add_argument("--pmc-kernel", default="gemv::gate_up_kernel")
     ap.add_argument("--pmc-copy-bytes", type=int, default=512 << 20)
     ap.add_argument("--pmc-bytes-per-launch", type=float, default=0.0)
     ap.add_argument("--command", nargs="*", default=[])

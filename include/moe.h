@@ -135,6 +135,21 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, int T, const moe_r
                 void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_route_permute -- moe_route followed by moe_permute in as few launches as possible (for
+ * batches of up to 64 tokens the top-k of every token and the permutation share one work-group).
+ * Arguments as in those two calls; the results are identical to calling them in sequence.
+ *   ws  device workspace of moe_route_permute_workspace_size() bytes; its first 256 bytes hold
+ *       the device error word read by moe_check_device_error
+ * ------------------------------------------------------------------------------------------ */
+size_t moe_route_permute_workspace_size(int T, const moe_routing* cfg, int S, int with_router_weights);
+int moe_route_permute(const void* x, int x_dtype, int T, int H, const float* w_router,
+                      const float* logits, const float* bias, const moe_routing* cfg,
+                      const int32_t* slot_map, int S, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* slot_offsets, int32_t* perm, int32_t* inv_perm,
+                      int32_t* miss_count, int32_t* miss_token, int32_t* miss_expert,
+                      float* miss_weight, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_expert_ffn -- y_perm[p] = FFN_{slot of p}(x[perm[p] / k]) for every resident position p.
  *
  *   w             weights descriptor (host struct, device pointers inside)
@@ -192,7 +207,7 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
 /* ------------------------------------------------------------------------------------------
  * helpers
  * ------------------------------------------------------------------------------------------ */
-/* Reads the error word at the start of a moe_permute / moe_layer workspace: synchronises
+/* Reads the error word at the start of a moe_permute / moe_route_permute / moe_layer workspace: synchronises
  * `stream`, returns MOE_OK, MOE_ERR_DEVICE (an out-of-range expert id or slot_map entry was
  * seen) or MOE_ERR_HIP. */
 int moe_check_device_error(const void* ws, void* stream);

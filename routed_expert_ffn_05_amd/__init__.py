@@ -51,6 +51,9 @@ _SIGS = {
     "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P, _R, _P, _P, _P, _P, _Z, _P]),
     "moe_permute_workspace_size": (_Z, [_I, _R, _I]),
     "moe_permute": (_I, [_P, _P, _I, _R, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_route_permute_workspace_size": (_Z, [_I, _R, _I, _I]),
+    "moe_route_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _R, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _P, _Z, _P]),
     "moe_expert_ffn_workspace_size": (_Z, [_W, _I, _I, _I, _I]),
     "moe_expert_ffn": (_I, [_W, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_gate_up": (_I, [_W, _P, _I, _I, _I, _P, _P, _I, _I, _P, _Z, _P]),
@@ -158,6 +161,20 @@ def moe_permute(topk_idx, topk_w, T, cfg, slot_map, S, counts, slot_offsets, per
                              _ptr(slot_offsets), _ptr(perm), _ptr(inv_perm), _ptr(miss_count),
                              _ptr(miss_token), _ptr(miss_expert), _ptr(miss_weight), _ptr(ws), ws_bytes,
                              _stream(stream)), "moe_permute")
+
+
+def moe_route_permute_workspace_size(T, cfg, S, with_router_weights) -> int:
+    return lib().moe_route_permute_workspace_size(T, _ref(cfg), S, int(bool(with_router_weights)))
+
+
+def moe_route_permute(x, x_dtype, T, H, w_router, logits, bias, cfg, slot_map, S, topk_idx, topk_w, counts,
+                      slot_offsets, perm, inv_perm, miss_count, miss_token, miss_expert, miss_weight, ws,
+                      ws_bytes, stream=None):
+    _check(lib().moe_route_permute(_ptr(x), x_dtype, T, H, _ptr(w_router), _ptr(logits), _ptr(bias), _ref(cfg),
+                                   _ptr(slot_map), S, _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+                                   _ptr(slot_offsets), _ptr(perm), _ptr(inv_perm), _ptr(miss_count),
+                                   _ptr(miss_token), _ptr(miss_expert), _ptr(miss_weight), _ptr(ws), ws_bytes,
+                                   _stream(stream)), "moe_route_permute")
 
 
 def moe_expert_ffn_workspace_size(w, T, k, path, mode) -> int:

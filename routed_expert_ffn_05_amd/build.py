@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_hip.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_abi.cpp", "router.hip", "permute.hip", "gemv.hip", "combine.hip"]
+SOURCES = ["moe_abi.cpp", "router.hip", "permute.hip", "gemv_dispatch.cpp", "gemv_f32.hip", "gemv_bf16.hip",
+           "gemv_fp8.hip", "gemv_mxfp4.hip", "combine.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -38,29 +39,31 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, src + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *lang, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *lang, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link ``out``; ``extra`` adds compiler flags (e.g. -D tuning
+    constants for an experimental build written elsewhere)."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 def main(argv=None) -> int:

@@ -78,6 +78,71 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // ---------------------------------------------------------------------------------------------
+// DPP reductions (GFX9 row shifts and row broadcasts; all 64 lanes must be active)
+// ---------------------------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_src(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_src_or(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Segmented sum: the total of each LPR-lane group (LPR = 16, 32 or 64) lands in its last lane.
+template <int LPR>
+__device__ __forceinline__ float seg_sum(float v) {
+  v += dpp_src<0x111>(v);  // row_shr:1
+  v += dpp_src<0x112>(v);  // row_shr:2
+  v += dpp_src<0x114>(v);  // row_shr:4
+  v += dpp_src<0x118>(v);  // row_shr:8   -> lane 15 of each 16-lane row holds the row sum
+  if constexpr (LPR >= 32) v += dpp_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  if constexpr (LPR >= 64) v += dpp_src<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Sum over the wave, returned to every lane.
+__device__ __forceinline__ float wave_total(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(seg_sum<64>(v)), 63));
+}
+
+// Max over the wave, returned to every lane.
+__device__ __forceinline__ float wave_max_all(float v) {
+  const float NEG = -__builtin_huge_valf();
+  auto step = [&](float o) { v = fmaxf(v, o); };
+  step(__int_as_float(dpp_src_or<0x111>(__float_as_int(NEG), __float_as_int(v))));
+  step(__int_as_float(dpp_src_or<0x112>(__float_as_int(NEG), __float_as_int(v))));
+  step(__int_as_float(dpp_src_or<0x114>(__float_as_int(NEG), __float_as_int(v))));
+  step(__int_as_float(dpp_src_or<0x118>(__float_as_int(NEG), __float_as_int(v))));
+  step(__int_as_float(dpp_src_or<0x142, 0xA>(__float_as_int(NEG), __float_as_int(v))));
+  step(__int_as_float(dpp_src_or<0x143, 0xC>(__float_as_int(NEG), __float_as_int(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Wave-wide best (value descending, index ascending); every lane receives the winner.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  const int NEG = __float_as_int(-__builtin_huge_valf());
+  const int BIG = 0x7FFFFFFF;
+#define MOE_ARGMAX_STEP(CTRL, RM)                                                 \
+  {                                                                               \
+    const float ov = __int_as_float(dpp_src_or<CTRL, RM>(NEG, __float_as_int(v))); \
+    const int oi = dpp_src_or<CTRL, RM>(BIG, i);                                  \
+    const bool take = ov > v || (ov == v && oi < i);                              \
+    v = take ? ov : v;                                                            \
+    i = take ? oi : i;                                                            \
+  }
+  MOE_ARGMAX_STEP(0x111, 0xF)
+  MOE_ARGMAX_STEP(0x112, 0xF)
+  MOE_ARGMAX_STEP(0x114, 0xF)
+  MOE_ARGMAX_STEP(0x118, 0xF)
+  MOE_ARGMAX_STEP(0x142, 0xA)
+  MOE_ARGMAX_STEP(0x143, 0xC)
+#undef MOE_ARGMAX_STEP
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// ---------------------------------------------------------------------------------------------
 // active-slot lookup: the ord-th slot with a non-empty row range in off[0..S]
 // (block-cooperative; every thread of the block gets the same answer, -1 if none)
 // ---------------------------------------------------------------------------------------------

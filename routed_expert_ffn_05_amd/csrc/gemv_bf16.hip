@@ -1,0 +1,13 @@
+// Decode GEMVs for bf16 expert weights (see gemv_impl.h).
+#define MOE_GEMV_WD moe::DT_BF16
+#include "gemv_impl.h"
+
+namespace moe {
+
+hipError_t launch_gemv_gate_up_bf16(const GemvArgs& g, hipStream_t st) {
+  return g.xdt == DT_F32 ? gemv::gate_up_dispatch<DT_BF16, DT_F32>(g, st) : gemv::gate_up_dispatch<DT_BF16, DT_BF16>(g, st);
+}
+
+hipError_t launch_gemv_down_bf16(const GemvArgs& g, hipStream_t st) { return gemv::down_dispatch<DT_BF16>(g, st); }
+
+}  // namespace moe

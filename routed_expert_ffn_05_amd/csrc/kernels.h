@@ -17,6 +17,13 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, i
                           int32_t* perm, int32_t* inv_perm, int32_t* miss_count,
                           int32_t* miss_token, int32_t* miss_expert, float* miss_weight,
                           uint32_t* err, hipStream_t st);
+// top-k of every token and the permutation in one work-group (small batches)
+size_t route_permute_lds_bytes(int T, int k, int E, int S);
+hipError_t launch_route_permute(const float* logits, const float* bias, int T, int k, int E,
+                                int score, int renorm, int32_t* idx, float* w,
+                                const int32_t* slot_map, int S, int32_t* counts, int32_t* off,
+                                int32_t* perm, int32_t* inv, int32_t* mc, int32_t* mt, int32_t* me,
+                                float* mw, uint32_t* err, hipStream_t st);
 
 struct GemvArgs {
   int wdt, xdt;

@@ -35,6 +35,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxDim = 8192;
 constexpr long long kMaxRows = 1LL << 26;  // T*k
+constexpr int kFusedRouteMaxT = 64;       // batches up to this size route and permute in one launch
 
 int elems_per_chunk(int wdtype) {
   switch (wdtype) {
@@ -322,10 +323,72 @@ int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_
 }
 
 // ---------------------------------------------------------------------------------------------
+size_t moe_route_permute_workspace_size(int T, const moe_routing* cfg, int S, int with_router_weights) {
+  (void)S;
+  return 256 + moe_route_workspace_size(T, cfg, with_router_weights);
+}
+
+int moe_route_permute(const void* x, int x_dtype, int T, int H, const float* w_router,
+                      const float* logits, const float* bias, const moe_routing* cfg,
+                      const int32_t* slot_map, int S, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* slot_offsets, int32_t* perm, int32_t* inv_perm,
+                      int32_t* miss_count, int32_t* miss_token, int32_t* miss_expert,
+                      float* miss_weight, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_routing(cfg));
+  MOE_TRY(check_T(T, cfg->k));
+  if ((w_router == nullptr) == (logits == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "exactly one of w_router / logits must be given");
+  if (S < 1 || S > cfg->E) return fail(MOE_ERR_INVALID_ARG, "S = %d must be in [1, E = %d]", S, cfg->E);
+  if (!slot_map && S != cfg->E) return fail(MOE_ERR_INVALID_ARG, "without slot_map S (%d) must equal E (%d)", S, cfg->E);
+  if (!counts || !slot_offsets) return fail(MOE_ERR_INVALID_ARG, "counts / slot_offsets is NULL");
+  if (T > 0 && (!topk_idx || !topk_w || !perm || !inv_perm))
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_w / perm / inv_perm is NULL");
+  if (slot_map && (!miss_count || !miss_token || !miss_expert || !miss_weight))
+    return fail(MOE_ERR_INVALID_ARG, "a slot_map needs miss_count, miss_token, miss_expert and miss_weight");
+  if (w_router) {
+    MOE_TRY(check_act_dtype(x_dtype, "x"));
+    if (H < 4 || H % 4) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 4", H);
+    if (T > 0 && !x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+    if (!aligned(x, 16) || !aligned(w_router, 16)) return fail(MOE_ERR_INVALID_ARG, "x / w_router must be 16-byte aligned");
+  }
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = moe_route_permute_workspace_size(T, cfg, S, w_router != nullptr);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (moe::permute_lds_bytes(cfg->E, S) > 160 * 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "E/S too large for the permutation kernel");
+  hipStream_t st = as_stream(stream);
+  uint32_t* err = static_cast<uint32_t*>(ws);
+  float* lbuf = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
+  hipError_t e = hipSuccess;
+  if (T > 0 && w_router) {
+    e = moe::launch_router_logits(x, x_dtype, w_router, bias, lbuf, T, H, cfg->E, st);
+    if (e != hipSuccess) return hip_fail(e, "router logits");
+  }
+  const float* lg = w_router ? lbuf : logits;
+  const float* tb = w_router ? nullptr : bias;  // with router weights the bias is already added
+  if (T > 0 && T <= kFusedRouteMaxT && moe::route_permute_lds_bytes(T, cfg->k, cfg->E, S) <= 160 * 1024) {
+    e = moe::launch_route_permute(lg, tb, T, cfg->k, cfg->E, cfg->score, cfg->renorm, topk_idx, topk_w,
+                                  slot_map, S, counts, slot_offsets, perm, inv_perm, miss_count, miss_token,
+                                  miss_expert, miss_weight, err, st);
+    if (e != hipSuccess) return hip_fail(e, "route+permute");
+    return MOE_OK;
+  }
+  if (T > 0) {
+    e = moe::launch_topk(lg, tb, tb ? 1 : 0, T, cfg->E, cfg->k, cfg->score, cfg->renorm, topk_idx, topk_w, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k");
+  }
+  e = moe::launch_permute(topk_idx, topk_w, T, cfg->k, cfg->E, slot_map, S, counts, slot_offsets, perm,
+                          inv_perm, miss_count, miss_token, miss_expert, miss_weight, err, st);
+  if (e != hipSuccess) return hip_fail(e, "permute");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
 namespace {
 struct LayerWs {
-  uint32_t* err;
-  float* logits;
+  void* rp;         // moe_route_permute workspace (error word first)
+  size_t rp_bytes;
   int32_t* topk_idx;
   float* topk_w;
   int32_t* counts;
@@ -343,8 +406,8 @@ LayerWs carve_layer(void* ws, int T, const moe_routing* cfg, const moe_weights* 
   Carve c(ws);
   LayerWs L{};
   const size_t R = size_t(T) * cfg->k;
-  L.err = c.take<uint32_t>(256);
-  L.logits = with_rw ? c.take<float>(size_t(T) * cfg->E * 4) : nullptr;
+  L.rp_bytes = moe_route_permute_workspace_size(T, cfg, w->S, with_rw);
+  L.rp = c.take<char>(L.rp_bytes);
   L.topk_idx = c.take<int32_t>(R * 4);
   L.topk_w = c.take<float>(R * 4);
   L.counts = c.take<int32_t>(size_t(cfg->E) * 4);
@@ -394,20 +457,12 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
   const int with_rw = w_router != nullptr;
   const size_t need = moe_layer_workspace_size(T, cfg, w, path, mode, with_rw);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
-  const size_t lds = moe::permute_lds_bytes(cfg->E, w->S);
-  if (lds > 160 * 1024) return fail(MOE_ERR_UNSUPPORTED, "E/S too large for the permutation kernel");
   LayerWs L = carve_layer(ws, T, cfg, w, rp, with_rw);
   int32_t* tidx = topk_idx ? topk_idx : L.topk_idx;
   float* tw = topk_w ? topk_w : L.topk_w;
-  hipStream_t st = as_stream(stream);
-  if (T > 0) {
-    MOE_TRY(moe_route(x, x_dtype, T, w->H, w_router, logits, bias, cfg, tidx, tw, L.logits,
-                      nullptr, 0, stream));
-  }
-  hipError_t e = moe::launch_permute(tidx, tw, T, cfg->k, cfg->E, slot_map, w->S, L.counts,
-                                     L.offsets, L.perm, L.inv, miss_count ? miss_count : L.miss_count,
-                                     miss_token, miss_expert, miss_weight, L.err, st);
-  if (e != hipSuccess) return hip_fail(e, "permute");
+  MOE_TRY(moe_route_permute(x, x_dtype, T, w->H, w_router, logits, bias, cfg, slot_map, w->S, tidx, tw,
+                            L.counts, L.offsets, L.perm, L.inv, miss_count ? miss_count : L.miss_count,
+                            miss_token, miss_expert, miss_weight, L.rp, L.rp_bytes, stream));
   if (T == 0) return MOE_OK;
   const size_t ffn_bytes = ffn_ws_size(w, T, cfg->k, rp);
   MOE_TRY(moe_expert_ffn(w, x, x_dtype, T, cfg->k, L.perm, L.offsets, rp, mode, L.y, L.ffn,

@@ -9,21 +9,29 @@
 //      base position for every key
 //   3. each wave walks its rows in chunks of 64 in order; rows of one chunk that share a key are
 //      ranked by lane order (ballot of equal keys, popcount below the lane)
+//
+// For small batches the top-k of every token runs in the same work-group first (one wave per
+// token), its results kept in LDS, so routing and permutation cost one launch.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int k, int E,
-    const int32_t* __restrict__ slot_map, int S, int32_t* __restrict__ counts,
-    int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
-    int32_t* __restrict__ miss_count, int32_t* __restrict__ miss_token,
-    int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight, uint32_t* __restrict__ err) {
-  extern __shared__ int32_t lds[];
+// LDS words used by permute_body
+__host__ __device__ inline size_t permute_lds_words(int E, int S) {
+  return size_t(kPermWaves) * (S + 1) + E + (S + 2);
+}
+
+__device__ void permute_body(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
+                             const int32_t* __restrict__ slot_map, int S, int32_t* __restrict__ counts,
+                             int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm,
+                             int32_t* __restrict__ inv_perm, int32_t* __restrict__ miss_count,
+                             int32_t* __restrict__ miss_token, int32_t* __restrict__ miss_expert,
+                             float* __restrict__ miss_weight, uint32_t* __restrict__ err, int32_t* lds) {
   const int K1 = S + 1;                     // keys: slots + the miss key
   int32_t* cnt = lds;                       // [kPermWaves][K1] per-wave counts, then bases
   int32_t* ecnt = cnt + kPermWaves * K1;    // [E]
@@ -45,7 +53,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   auto key_of = [&](int r, int& e) -> int {
     e = topk_idx[r];
     if (e < 0 || e >= E) return -1;
-    int s = slot_map ? slot_map[e] : e;
+    const int s = slot_map ? slot_map[e] : e;
     if (s < -1 || s >= S) return -1;
     return s < 0 ? S : s;
   };
@@ -77,7 +85,6 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int a = tid * per, b = min(S, a + per);
     int local = 0;
     for (int i = a; i < b; ++i) local += tot[i];
-    // inclusive wave scan of `local`
     int incl = local;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -155,8 +162,57 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
 }
 
-size_t permute_lds_bytes(int E, int S) {
-  return sizeof(int32_t) * (size_t(kPermWaves) * (S + 1) + E + (S + 2));
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int k, int E,
+    const int32_t* __restrict__ slot_map, int S, int32_t* __restrict__ counts,
+    int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ miss_count, int32_t* __restrict__ miss_token,
+    int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight, uint32_t* __restrict__ err) {
+  extern __shared__ int32_t lds[];
+  permute_body(topk_idx, topk_w, T, k, E, slot_map, S, counts, slot_offsets, perm, inv_perm,
+               miss_count, miss_token, miss_expert, miss_weight, err, lds);
+}
+
+// top-k of every token (one wave each), then the permutation, in one work-group
+template <int VPL>
+__global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int k, int E, int score,
+    int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    const int32_t* __restrict__ slot_map, int S, int32_t* __restrict__ counts,
+    int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ miss_count, int32_t* __restrict__ miss_token,
+    int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight, uint32_t* __restrict__ err) {
+  extern __shared__ int32_t lds[];
+  const int R = T * k;
+  int32_t* sidx = lds;                                   // [R]
+  float* sw = reinterpret_cast<float*>(lds + R);         // [R]
+  int32_t* scratch = lds + 2 * R;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  for (int t = wid; t < T; t += kPermWaves) {
+    int my_e;
+    float my_w;
+    topk_wave<VPL>(logits + size_t(t) * E, bias, E, k, score, renorm, my_e, my_w);
+    if (lane < k) {
+      sidx[t * k + lane] = my_e;
+      sw[t * k + lane] = my_w;
+      topk_idx[size_t(t) * k + lane] = my_e;
+      topk_w[size_t(t) * k + lane] = my_w;
+    }
+  }
+  __syncthreads();
+  permute_body(sidx, sw, T, k, E, slot_map, S, counts, slot_offsets, perm, inv_perm, miss_count,
+               miss_token, miss_expert, miss_weight, err, scratch);
+}
+
+size_t permute_lds_bytes(int E, int S) { return sizeof(int32_t) * permute_lds_words(E, S); }
+
+size_t route_permute_lds_bytes(int T, int k, int E, int S) {
+  return sizeof(int32_t) * (size_t(2) * T * k + permute_lds_words(E, S));
+}
+
+static hipError_t set_lds(const void* kern, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
 }
 
 hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
@@ -165,10 +221,41 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, i
                           int32_t* miss_token, int32_t* miss_expert, float* miss_weight,
                           uint32_t* err, hipStream_t st) {
   const size_t lds = permute_lds_bytes(E, S);
+  hipError_t e = set_lds((const void*)permute_kernel, lds);
+  if (e != hipSuccess) return e;
   permute_kernel<<<1, kPermThreads, lds, st>>>(topk_idx, topk_w, T, k, E, slot_map, S, counts,
                                                slot_offsets, perm, inv_perm, miss_count,
                                                miss_token, miss_expert, miss_weight, err);
   return hipGetLastError();
+}
+
+template <int VPL>
+static hipError_t launch_rp(const float* logits, const float* bias, int T, int k, int E, int score,
+                            int renorm, int32_t* idx, float* w, const int32_t* slot_map, int S,
+                            int32_t* counts, int32_t* off, int32_t* perm, int32_t* inv, int32_t* mc,
+                            int32_t* mt, int32_t* me, float* mw, uint32_t* err, hipStream_t st) {
+  const size_t lds = route_permute_lds_bytes(T, k, E, S);
+  hipError_t e = set_lds((const void*)route_permute_kernel<VPL>, lds);
+  if (e != hipSuccess) return e;
+  route_permute_kernel<VPL><<<1, kPermThreads, lds, st>>>(logits, bias, T, k, E, score, renorm, idx, w,
+                                                          slot_map, S, counts, off, perm, inv, mc, mt,
+                                                          me, mw, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const float* logits, const float* bias, int T, int k, int E,
+                                int score, int renorm, int32_t* idx, float* w,
+                                const int32_t* slot_map, int S, int32_t* counts, int32_t* off,
+                                int32_t* perm, int32_t* inv, int32_t* mc, int32_t* mt, int32_t* me,
+                                float* mw, uint32_t* err, hipStream_t st) {
+  const int vpl = (E + 63) / 64;
+  if (vpl <= 2)
+    return launch_rp<2>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);
+  if (vpl <= 4)
+    return launch_rp<4>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);
+  if (vpl <= 8)
+    return launch_rp<8>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);
+  return launch_rp<16>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);
 }
 
 }  // namespace moe

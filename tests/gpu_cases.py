@@ -122,6 +122,38 @@ class GpuCase:
                     inv_perm=D.to_host(inv)[:R], miss_count=n_miss, miss_token=D.to_host(mt)[:n_miss],
                     miss_expert=D.to_host(me)[:n_miss], miss_weight=D.to_host(mw)[:n_miss])
 
+    def route_permute(self):
+        torch = self.torch
+        c = self.cfg
+        R = c.T * c.k
+        idx = torch.empty((max(c.T, 1), c.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((max(c.T, 1), c.k), dtype=torch.float32, device="cuda")
+        counts = torch.empty(c.E, dtype=torch.int32, device="cuda")
+        off = torch.empty(c.S + 1, dtype=torch.int32, device="cuda")
+        perm = torch.empty(max(R, 1), dtype=torch.int32, device="cuda")
+        inv = torch.empty(max(R, 1), dtype=torch.int32, device="cuda")
+        mc = torch.zeros(1, dtype=torch.int32, device="cuda")
+        mt = torch.empty(max(R, 1), dtype=torch.int32, device="cuda")
+        me = torch.empty(max(R, 1), dtype=torch.int32, device="cuda")
+        mw = torch.empty(max(R, 1), dtype=torch.float32, device="cuda")
+        nb = moe.moe_route_permute_workspace_size(c.T, self.route_cfg, c.S, self.w_router is not None)
+        ws = D.workspace(nb)
+        sm = self.slot_map
+        moe.moe_route_permute(self.x, self.xdt, c.T, c.H, self.w_router, self.logits, self.bias, self.route_cfg, sm,
+                              c.S, idx, w, counts, off, perm, inv, mc if sm is not None else None,
+                              mt if sm is not None else None, me if sm is not None else None,
+                              mw if sm is not None else None, ws, nb)
+        torch.cuda.synchronize()
+        moe.moe_check_device_error(ws)
+        n_res = int(D.to_host(off)[-1])
+        n_miss = int(D.to_host(mc)[0]) if sm is not None else 0
+        res = dict(topk_idx=D.to_host(idx)[: c.T], topk_w=D.to_host(w)[: c.T], counts=D.to_host(counts),
+                   slot_offsets=D.to_host(off), perm=D.to_host(perm)[:n_res], inv_perm=D.to_host(inv)[:R])
+        if sm is not None:
+            res.update(miss_count=n_miss, miss_token=D.to_host(mt)[:n_miss], miss_expert=D.to_host(me)[:n_miss],
+                       miss_weight=D.to_host(mw)[:n_miss])
+        return res
+
     def expert_ffn(self, perm, slot_offsets, path=moe.MOE_PATH_AUTO, mode=moe.MOE_MODE_A):
         torch = self.torch
         c = self.cfg

@@ -63,6 +63,17 @@ def test_permute_stage(small_case):
     check_permute(res, ref)
 
 
+def test_route_permute_stage(small_case):
+    # one launch for T <= 64 (top-k and permutation share a work-group), two above
+    from gpu_cases import check_permute, check_routing
+    name, inp, g, ref = small_case
+    _banner(name + "/route_permute", inp.cfg)
+    res = g.route_permute()
+    flipped = check_routing(res["topk_idx"], res["topk_w"], ref)
+    if not flipped:
+        check_permute(res, ref)
+
+
 def test_expert_ffn_stage(small_case):
     import routed_expert_ffn_05_amd as moe
     from gpu_cases import assert_fp_close

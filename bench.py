@@ -247,9 +247,15 @@ def run(args):
     slot_bytes_d = (w.w_d.numel() * w.w_d.element_size() + (0 if w.s_d is None else w.s_d.numel() * w.s_d.element_size())) // S
     xb = 2 if cfg.xdtype == "bf16" else 4
 
+    gemm = path == moe.MOE_PATH_GEMM or (path == moe.MOE_PATH_AUTO and cfg.wdtype != "f32" and H % 64 == 0
+                                         and I % 64 == 0 and T * k > 4 * S)
+
     def gate_up_bytes(r):
         touched, n_res = per_rot[r]
-        return touched * slot_bytes_gu + T * H * xb + n_res * I * 4
+        return touched * slot_bytes_gu + T * H * xb + n_res * I * (2 if gemm else 4)
+
+    def gate_up_flops(r):
+        return per_rot[r][1] * 2.0 * H * 2 * I
 
     def layer_bytes(r):
         touched, n_res = per_rot[r]
@@ -278,7 +284,8 @@ def run(args):
     achieved = sum(gu_bytes) / (sum(gu_ms) / 1e3) / 1e9
     layer_gbs = sum(layer_bytes(i % len(rot)) for i in range(args.steps)) / (total_ms / 1e3) / 1e9
     log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step), "
-        f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s")
+        f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s; "
+        f"path {'gemm' if gemm else 'gemv'}")
 
     # the staged step is moe_layer's own sequence: check one rotation bit for bit
     lay = D.Layer(T=T, H=H, I=I, E=E, k=k, score=cfg.score, renorm=cfg.renorm, xdtype=cfg.xdtype,
@@ -303,10 +310,15 @@ def run(args):
 
     key = f"{cfg.name}_T{T}"
     traffic = recorded_traffic(key)
+    tflops = sum(gate_up_flops(i % len(rot)) for i in range(args.steps)) / (sum(gu_ms) / 1e3) / 1e12
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "moe::gemv::gate_up_kernel", "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
+                "kernel": "moe::gemm::gemm_kernel (gate/up)" if gemm else "moe::gemv::gate_up_kernel",
+                "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
                 "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2)}
+    if gemm:
+        roofline["mfma_tflops"] = round(tflops, 1)
+        roofline["mfma_frac_of_bf16_peak"] = round(tflops / MFMA_PEAK_TFLOPS["bf16"], 4)
 
     cpu = None
     if args.cpu_baseline:

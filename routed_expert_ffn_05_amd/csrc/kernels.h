@@ -42,6 +42,29 @@ struct GemvArgs {
 hipError_t launch_gemv_gate_up(const GemvArgs& g, hipStream_t st);
 hipError_t launch_gemv_down(const GemvArgs& g, hipStream_t st);
 
+struct GemmArgs {
+  int wdt, xdt;
+  int S, T, k, H, I;
+  const void* w_gu;
+  const void* s_gu;
+  const void* w_d;
+  const void* s_d;
+  const void* x;        // [T, H] bf16 (or fp32, rounded to bf16 when staged)
+  const int32_t* perm;
+  const int32_t* off;
+  void* a;              // [T*k, I] bf16
+  float* y;             // [T*k, H] fp32
+  int2* tiles_gu;       // tile lists written by the scheduler
+  int2* tiles_dn;
+  int32_t* counts;      // [2]: tiles of each GEMM
+};
+size_t gemm_tiles_max(int T, int k, int S, int nt);
+int gemm_nt_gate_up(int I);
+int gemm_nt_down(int H);
+hipError_t launch_gemm_schedule(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t st);
+
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int T, int k, int H,
                           void* out, int odt, hipStream_t st);
 

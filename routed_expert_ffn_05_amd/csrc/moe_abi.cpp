@@ -93,18 +93,26 @@ int check_weights(const moe_weights* w) {
   return MOE_OK;
 }
 
-int resolve_path(int path, int T, int k, int S) {
-  (void)T; (void)k; (void)S;
-  if (path == MOE_PATH_AUTO) return MOE_PATH_GEMV;
-  return path;
+// the matrix-core path needs bf16-exact weights and K-steps of 64
+bool gemm_capable(const moe_weights* w) {
+  return w->wdtype != MOE_F32 && w->H % 64 == 0 && w->I % 64 == 0;
 }
 
-int check_path_mode(int path, int mode) {
+// AUTO: the GEMM path once slots hold several rows on average (measured crossover: the GEMV
+// streams weights at the same rate but re-reads them per group of rows)
+int resolve_path(int path, int T, int k, const moe_weights* w) {
+  if (path != MOE_PATH_AUTO) return path;
+  if (gemm_capable(w) && (long long)T * k > 4LL * w->S) return MOE_PATH_GEMM;
+  return MOE_PATH_GEMV;
+}
+
+int check_path_mode(int path, int mode, const moe_weights* w) {
   if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_GEMM)
     return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
   if (mode != MOE_MODE_A && mode != MOE_MODE_B) return fail(MOE_ERR_INVALID_ARG, "unknown mode %d", mode);
-  if (path == MOE_PATH_GEMM) return fail(MOE_ERR_UNSUPPORTED, "the GEMM path is not available in this build");
-  if (mode == MOE_MODE_B) return fail(MOE_ERR_UNSUPPORTED, "mode B needs the GEMM path");
+  if (path == MOE_PATH_GEMM && !gemm_capable(w))
+    return fail(MOE_ERR_UNSUPPORTED, "the GEMM path needs bf16, FP8 or MXFP4 weights and H, I multiples of 64");
+  if (mode == MOE_MODE_B) return fail(MOE_ERR_UNSUPPORTED, "mode B is not available in this build");
   return MOE_OK;
 }
 
@@ -121,9 +129,28 @@ struct Carve {
   }
 };
 
+// expert-FFN workspace: [256: header][a: T*k*I fp32 (GEMV) or bf16 (GEMM)][tile lists][counts]
+struct FfnWs {
+  void* a;
+  int2* tiles_gu;
+  int2* tiles_dn;
+  int32_t* counts;
+  size_t used;
+};
+FfnWs carve_ffn(void* ws, const moe_weights* w, int T, int k) {
+  Carve c(ws);
+  FfnWs f{};
+  c.take<char>(256);
+  f.a = c.take<char>(size_t(T) * k * w->I * sizeof(float));
+  f.tiles_gu = c.take<int2>(moe::gemm_tiles_max(T, k, w->S, moe::gemm_nt_gate_up(w->I)) * sizeof(int2));
+  f.tiles_dn = c.take<int2>(moe::gemm_tiles_max(T, k, w->S, moe::gemm_nt_down(w->H)) * sizeof(int2));
+  f.counts = c.take<int32_t>(2 * sizeof(int32_t));
+  f.used = c.used;
+  return f;
+}
 size_t ffn_ws_size(const moe_weights* w, int T, int k, int path) {
   (void)path;
-  return 256 + align256(size_t(T) * k * w->I * sizeof(float));
+  return carve_ffn(nullptr, w, T, k).used;
 }
 
 #define MOE_TRY(expr)           \
@@ -228,7 +255,7 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, int T, const moe_r
 size_t moe_expert_ffn_workspace_size(const moe_weights* w, int T, int k, int path, int mode) {
   (void)mode;
   if (!w || T < 0 || k < 1 || w->I < 1) return 0;
-  return ffn_ws_size(w, T, k, resolve_path(path, T, k, w->S));
+  return ffn_ws_size(w, T, k, resolve_path(path, T, k, w));
 }
 
 namespace {
@@ -238,7 +265,7 @@ int check_ffn_common(const moe_weights* w, int T, int k, const int32_t* slot_off
   MOE_TRY(check_weights(w));
   if (k < 1 || k > kMaxK) return fail(MOE_ERR_INVALID_ARG, "k = %d out of range", k);
   MOE_TRY(check_T(T, k));
-  MOE_TRY(check_path_mode(path, mode));
+  MOE_TRY(check_path_mode(path, mode, w));
   if (!slot_offsets) return fail(MOE_ERR_INVALID_ARG, "slot_offsets is NULL");
   if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -266,8 +293,34 @@ moe::GemvArgs gemv_args(const moe_weights* w, const void* x, int x_dtype, int T,
   g.x = x;
   g.perm = perm;
   g.off = off;
-  g.a = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
+  g.a = static_cast<float*>(carve_ffn(ws, w, T, k).a);
   g.y = y;
+  return g;
+}
+
+moe::GemmArgs gemm_args(const moe_weights* w, const void* x, int x_dtype, int T, int k,
+                        const int32_t* perm, const int32_t* off, float* y, void* ws) {
+  const FfnWs f = carve_ffn(ws, w, T, k);
+  moe::GemmArgs g{};
+  g.wdt = w->wdtype;
+  g.xdt = x_dtype;
+  g.S = w->S;
+  g.T = T;
+  g.k = k;
+  g.H = w->H;
+  g.I = w->I;
+  g.w_gu = w->w_gu;
+  g.s_gu = w->s_gu;
+  g.w_d = w->w_d;
+  g.s_d = w->s_d;
+  g.x = x;
+  g.perm = perm;
+  g.off = off;
+  g.a = f.a;
+  g.y = y;
+  g.tiles_gu = f.tiles_gu;
+  g.tiles_dn = f.tiles_dn;
+  g.counts = f.counts;
   return g;
 }
 
@@ -281,6 +334,13 @@ int moe_expert_gate_up(const moe_weights* w, const void* x, int x_dtype, int T, 
   if (T > 0 && (!x || !perm)) return fail(MOE_ERR_INVALID_ARG, "x / perm is NULL");
   if (!aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned");
   if (T == 0) return MOE_OK;
+  if (resolve_path(path, T, k, w) == MOE_PATH_GEMM) {
+    moe::GemmArgs g = gemm_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws);
+    hipError_t e = moe::launch_gemm_schedule(g, as_stream(stream));
+    if (e == hipSuccess) e = moe::launch_gemm_gate_up(g, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "gate/up GEMM");
+    return MOE_OK;
+  }
   moe::GemvArgs g = gemv_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws);
   hipError_t e = moe::launch_gemv_gate_up(g, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMV");
@@ -293,6 +353,12 @@ int moe_expert_down(const moe_weights* w, int T, int k, const int32_t* slot_offs
   if (T > 0 && !y_perm) return fail(MOE_ERR_INVALID_ARG, "y_perm is NULL");
   if (!aligned(y_perm, 16)) return fail(MOE_ERR_INVALID_ARG, "y_perm must be 16-byte aligned");
   if (T == 0) return MOE_OK;
+  if (resolve_path(path, T, k, w) == MOE_PATH_GEMM) {
+    moe::GemmArgs g = gemm_args(w, nullptr, MOE_BF16, T, k, nullptr, slot_offsets, y_perm, ws);
+    hipError_t e = moe::launch_gemm_down(g, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "down GEMM");
+    return MOE_OK;
+  }
   moe::GemvArgs g = gemv_args(w, nullptr, MOE_F32, T, k, nullptr, slot_offsets, y_perm, ws);
   hipError_t e = moe::launch_gemv_down(g, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "down GEMV");
@@ -426,7 +492,7 @@ size_t moe_layer_workspace_size(int T, const moe_routing* cfg, const moe_weights
                                 int mode, int with_router_weights) {
   (void)mode;
   if (!cfg || !w || T < 0 || cfg->k < 1 || cfg->E < 1) return 0;
-  return carve_layer(nullptr, T, cfg, w, resolve_path(path, T, cfg->k, w->S), with_router_weights).used;
+  return carve_layer(nullptr, T, cfg, w, resolve_path(path, T, cfg->k, w), with_router_weights).used;
 }
 
 int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const float* logits,
@@ -438,7 +504,7 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
   MOE_TRY(check_routing(cfg));
   MOE_TRY(check_T(T, cfg->k));
   MOE_TRY(check_weights(w));
-  MOE_TRY(check_path_mode(path, mode));
+  MOE_TRY(check_path_mode(path, mode, w));
   MOE_TRY(check_act_dtype(x_dtype, "x"));
   MOE_TRY(check_act_dtype(out_dtype, "out"));
   if (!slot_map && w->S != cfg->E) return fail(MOE_ERR_INVALID_ARG, "without slot_map S (%d) must equal E (%d)", w->S, cfg->E);
@@ -453,7 +519,7 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
   if (!aligned(x, 16) || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "x / out must be 16-byte aligned");
   if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const int rp = resolve_path(path, T, cfg->k, w->S);
+  const int rp = resolve_path(path, T, cfg->k, w);
   const int with_rw = w_router != nullptr;
   const size_t need = moe_layer_workspace_size(T, cfg, w, path, mode, with_rw);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);

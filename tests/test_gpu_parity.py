@@ -20,7 +20,16 @@ SMALL = {
     "fp8_zipf": gen.config("prefill_fp8_zipf", T=300, H=256, E=32, I=128, k=8),
     "mxfp4_compact": gen.config("compact_mxfp4", T=53, H=512, E=40, I=160, k=6, resident=13),
     "mxfp4_compact_t1": gen.config("compact_mxfp4", T=1, H=256, E=16, I=128, k=4, resident=5),
+    # shapes for the matrix-core path (H, I multiples of 64): several M tiles per slot, FP8 up rows
+    # straddling 128-row scale blocks (I % 128 == 64), ragged 32-row blocks
+    "bf16_gemm": gen.config("decode_bf16", T=70, H=512, E=12, I=192, k=4),
+    "fp8_big_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=8, I=320, k=2),
+    "mxfp4_gemm_compact": gen.config("compact_mxfp4", T=200, H=512, E=24, I=192, k=6, resident=9),
 }
+
+
+def _gemm_capable(cfg):
+    return cfg.wdtype != "f32" and cfg.H % 64 == 0 and cfg.I % 64 == 0
 
 
 def _gpu():
@@ -74,13 +83,20 @@ def test_route_permute_stage(small_case):
         check_permute(res, ref)
 
 
-def test_expert_ffn_stage(small_case):
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+def test_expert_ffn_stage(small_case, path):
     import routed_expert_ffn_05_amd as moe
     from gpu_cases import assert_fp_close
     name, inp, g, ref = small_case
-    _banner(name + "/expert_ffn", inp.cfg)
-    y = g.expert_ffn(ref["perm"], ref["slot_offsets"], path=moe.MOE_PATH_GEMV)
-    assert_fp_close(y, ref["y_perm"], f"{name} y_perm (GEMV)")
+    _banner(f"{name}/expert_ffn/{path}", inp.cfg)
+    p = moe.MOE_PATH_GEMV if path == "gemv" else moe.MOE_PATH_GEMM
+    if path == "gemm" and not _gemm_capable(inp.cfg):
+        with pytest.raises(moe.MoeError) as ei:
+            g.expert_ffn(ref["perm"], ref["slot_offsets"], path=p)
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+        return
+    y = g.expert_ffn(ref["perm"], ref["slot_offsets"], path=p)
+    assert_fp_close(y, ref["y_perm"], f"{name} y_perm ({path})")
 
 
 def test_combine_stage(small_case):
@@ -91,11 +107,15 @@ def test_combine_stage(small_case):
     assert_fp_close(out, ref["out"], f"{name} combine")
 
 
-def test_layer(small_case):
+@pytest.mark.parametrize("path", ["auto", "gemv", "gemm"])
+def test_layer(small_case, path):
+    import routed_expert_ffn_05_amd as moe
     from gpu_cases import assert_fp_close, check_misses, check_routing
     name, inp, g, ref = small_case
-    _banner(name + "/layer", inp.cfg)
-    res = g.layer()
+    _banner(f"{name}/layer/{path}", inp.cfg)
+    if path == "gemm" and not _gemm_capable(inp.cfg):
+        pytest.skip("shape outside the matrix-core path (covered by the UNSUPPORTED check)")
+    res = g.layer(path={"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[path])
     flipped = check_routing(res["topk_idx"], res["topk_w"], ref)
     keep = np.array([t not in flipped for t in range(inp.cfg.T)], bool)
     assert_fp_close(res["out"][keep], ref["out"][keep], f"{name} layer out")

@@ -5,20 +5,26 @@
 //
 // Tiles.  A work-group computes a BM x BN output tile of one slot with 4 waves side by side along
 // N (32 columns each) and up to 4 MFMA row blocks of 32 rows; a tile whose slot has fewer rows
-// skips the empty row blocks, so a slot of n rows costs ceil(n/32) row blocks of matrix work while
-// its weights are streamed once per 128-row M-tile.  K advances in steps of BK = 64 through two
-// LDS stages (global loads of step k+1 are in flight while step k runs on the matrix cores).
-//   * activations (bf16) are gathered row by row through the permutation and copied to LDS;
-//   * weights are decoded exactly into bf16 while being staged: e4m3fn values are bf16-exact,
-//     e2m1 times a power-of-two E8M0 scale is bf16-exact (the conversion applies the scale);
-//   * an FP8 128x128 block scale is constant over a wave's 32 columns and a 128-wide K block, so
-//     each wave accumulates a K block in a temporary and adds scale * temporary to the result;
-//   * gate/up: the N tile holds 64 gate rows then the 64 matching up rows; wave w reads its 32
-//     MFMA columns as gate rows 16w..16w+15 followed by up rows 16w..16w+15, so each lane pair
-//     (l, l+16) holds gate and up of the same (row, i) and SiLU(g)*u is formed in registers.
-// Scheduling.  A one-work-group kernel lists the tiles in (slot, N tile, M tile) order; tile
-// blocks are mapped XCD-major (block b runs on XCD b % 8), so the M tiles that share a weight tile
-// run back to back on one XCD and find it in that XCD's L2.
+// runs only ceil(rows/32) row blocks, so a slot of n rows costs that much matrix work while its
+// weights are streamed once per 128-row M tile.
+// Staging.  Operand tiles of each K step (BK = 64) move from HBM to LDS by direct LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane) with no register
+// staging; one explicit vmcnt wait and one barrier per step.  A stage holds the A rows the tile
+// uses plus the B tile, so tiles with fewer row blocks keep more K steps in flight within the same
+// LDS budget (2 to 6 stages).  Within a row, the
+// 16-byte granule g of row r is stored at slot g ^ f(r) (f spreads 16 consecutive rows over
+// distinct bank groups for the MFMA fragment reads).  Weights stay in their stored format in LDS
+// and are decoded when a B fragment is read: e4m3fn -> bf16 is exact; e2m1 times a power-of-two
+// E8M0 scale -> bf16 is exact (the conversion applies the scale).
+// FP8 block scales.  A 128x128 block scale is constant over a lane's column and a 128-wide K
+// block: each lane accumulates a K block in a temporary and adds scale * temporary to the result.
+// Gate/up fusion.  The N tile holds 64 gate rows then the 64 matching up rows; wave w reads its
+// 32 MFMA columns as gate rows 16w..16w+15 followed by up rows 16w..16w+15, so lanes l and l+16
+// hold gate and up of the same (row, i) and SiLU(g)*u is formed in registers.
+// Scheduling.  A one-work-group kernel lists the tiles in (slot, M tile, N tile) order; blocks are
+// mapped XCD-major (block b runs on XCD b % 8), so the tiles co-resident on one XCD are the N
+// tiles of a few M tiles of one slot: each activation slice is read from L2 by all N tiles, each
+// weight slice by the few M tiles in flight.
 #include <type_traits>
 
 #include "common.h"
@@ -29,10 +35,23 @@ namespace gemm {
 
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kStride = BK + 8;  // bf16 per LDS row: 16-byte pad against bank conflicts
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// B operand bytes per row and K step, stages in flight
+template <int WD> struct BFmt {
+  static constexpr int ROW = WD == DT_BF16 ? 128 : WD == DT_FP8 ? 64 : 32;
+  static constexpr int STAGE = BN * ROW;
+  static constexpr int INSTR = STAGE / 4096;  // 1 KiB direct loads per wave and step
+  // LDS for the stages (two work-groups per CU with the format's other LDS data)
+  static constexpr int BUDGET = WD == DT_BF16 ? 64 * 1024 : WD == DT_FP8 ? 72 * 1024 : 60 * 1024;
+  // a K step of a tile with NS row blocks occupies NS*4 KiB of A plus the B tile; as many steps
+  // are kept in flight as the budget holds (at most 6)
+  static constexpr int stage_bytes(int ns) { return ns * 4096 + STAGE; }
+  static constexpr int nstage(int ns) { return BUDGET / stage_bytes(ns) < 6 ? BUDGET / stage_bytes(ns) : 6; }
+};
 
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   const int x = b & 7, j = b >> 3;
@@ -41,32 +60,28 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return base + j;
 }
 
-// 16 e4m3fn codes -> 16 bf16 (exact), written as two 16-byte words
-__device__ __forceinline__ void fp8x16_to_bf16(const uint4 q, uint4& lo, uint4& hi) {
-  const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[i], 1.0f, false);
-    auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[i], 1.0f, true);
-    o[2 * i] = __builtin_bit_cast(uint32_t, a);
-    o[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
-  }
-  lo = make_uint4(o[0], o[1], o[2], o[3]);
-  hi = make_uint4(o[4], o[5], o[6], o[7]);
+// 16 bytes per lane from `src` into LDS at (wave-uniform) lds + 16*lane.  Written as inline
+// assembly so that the compiler's wait insertion does not treat it as aliasing every LDS read:
+// the kernel orders these loads itself (explicit vmcnt waits and barriers), and no other vector
+// memory load is in flight while they are.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(uint32_t(size_t((lds_void*)lds)));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m), "v"(src) : "memory", "m0");
 }
 
-// 32 e2m1 codes times `scale` (power of two) -> 32 bf16 (exact), four 16-byte words
-__device__ __forceinline__ void fp4x32_to_bf16(const uint4 q, float scale, uint4 (&o)[4]) {
-  const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u[i], scale, 0));
-    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u[i], scale, 1));
-    const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u[i], scale, 2));
-    const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u[i], scale, 3));
-    o[i] = make_uint4(a, b, c, d);
-  }
+// swizzled position of 16-byte granule g in a row r of a 128-byte (bf16) tile row
+__device__ __forceinline__ int swz128(int r, int g) { return g ^ ((r >> 1) & 7); }
+// 64-byte rows (fp8)
+__device__ __forceinline__ int swz64(int r, int g) { return g ^ ((r >> 2) & 3); }
+// 32-byte rows (fp4)
+__device__ __forceinline__ int swz32(int r, int g) { return g ^ ((r >> 3) & 1); }
+
+// s_waitcnt vmcnt(n) lgkmcnt(0), expcnt unconstrained (gfx9 encoding).  lgkmcnt(0) makes this
+// wave's LDS reads of earlier steps complete before the barrier that lets a stage be reloaded.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
 template <int WD>
@@ -74,17 +89,22 @@ __host__ __device__ constexpr size_t row_bytes(int K) {
   return WD == DT_BF16 ? size_t(K) * 2 : WD == DT_FP8 ? size_t(K) : size_t(K) / 2;
 }
 
+constexpr int kMaxFp4Kb = 128;  // MXFP4: E8M0 scales per row staged in LDS (K <= 4096)
+
 // ---------------------------------------------------------------------------------------------
 // GATEUP = true:  A = x rows (through perm), B = W_gu[s] (gate/up interleaved), out a (bf16)
 // GATEUP = false: A = a rows (positions),    B = W_d[s],                        out y (fp32)
 // ---------------------------------------------------------------------------------------------
-template <int WD, bool GATEUP, int XT = DT_BF16>
+template <int WD, bool GATEUP>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
-    const uint8_t* __restrict__ w, const void* __restrict__ wscale, const void* __restrict__ act,
+    const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ off, const int2* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, int T, int k, int K, int N, int I, void* __restrict__ out) {
-  __shared__ __align__(16) uint16_t As[2][BM * kStride];
-  __shared__ __align__(16) uint16_t Bs[2][BN * kStride];
+  using F = BFmt<WD>;
+  __shared__ __align__(16) uint8_t smem[F::BUDGET];
+  __shared__ float Ssc[3][64];                                    // FP8 block scales
+  __shared__ __align__(16) uint8_t Sfp4[WD == DT_MXFP4 ? BN * kMaxFp4Kb : 16];  // MXFP4 scales
+  __shared__ uint8_t rowok[BM];
   const int n_act = ntiles[0];
   if (int(blockIdx.x) >= n_act) return;
   const int2 ent = tiles[xcd_remap(blockIdx.x, n_act)];
@@ -101,179 +121,183 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
   const int n0 = GATEUP ? nt * (BN / 2) : nt * BN;
   const size_t rb = row_bytes<WD>(K);
   const uint8_t* wslot = w + size_t(s) * N * rb;
-
-  // ---- global -> register assignments --------------------------------------------------------
-  // A: 128 rows x 64 bf16 = 1024 16-byte granules, 4 per thread: row (tid>>3) + 32*i, granule tid&7
-  // (fp32 activations are rounded to bf16, nearest even, as they are staged)
-  const uint8_t* arow[4];
-  bool aok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    aok[i] = r < rows;
-    int src = 0;
-    if (aok[i]) {
-      if constexpr (GATEUP) {
-        const int rr = perm[m0 + r];
-        src = rr / k;
-        aok[i] = rr >= 0 && src < T;
-      } else {
-        src = m0 + r;
-      }
-    }
-    constexpr int XB = XT == DT_F32 ? 4 : 2;
-    arow[i] = static_cast<const uint8_t*>(act) + (size_t(aok[i] ? src : 0) * K + (tid & 7) * 8) * XB;
-  }
-  // B rows of the tile in LDS order
   auto brow_global = [&](int r) -> int {
     if constexpr (GATEUP) return r < 64 ? n0 + r : I + n0 + (r - 64);
     return n0 + r;
   };
-  // B granules per thread: bf16 4 (row (tid>>3)+32i, 8 elements), fp8 2 (row (tid>>2)+64i,
-  // 16 elements), fp4 1 (row tid>>1, 32 elements)
-  constexpr int NBG = WD == DT_BF16 ? 4 : WD == DT_FP8 ? 2 : 1;
-  int brow[NBG], bcol[NBG];
-  bool bok[NBG];
-#pragma unroll
-  for (int i = 0; i < NBG; ++i) {
-    int r, c;
-    if constexpr (WD == DT_BF16) {
-      r = (tid >> 3) + 32 * i;
-      c = (tid & 7) * 8;
-    } else if constexpr (WD == DT_FP8) {
-      r = (tid >> 2) + 64 * i;
-      c = (tid & 3) * 16;
-    } else {
-      r = tid >> 1;
-      c = (tid & 1) * 32;
-    }
-    const int g = brow_global(r);
-    bok[i] = g < N;
-    brow[i] = r;
-    bcol[i] = c;
-  }
-  const uint8_t* bsrc[NBG];
-#pragma unroll
-  for (int i = 0; i < NBG; ++i) {
-    const int g = bok[i] ? brow_global(brow[i]) : 0;
-    bsrc[i] = wslot + size_t(g) * rb;
-  }
-  const uint8_t* s_fp4 = nullptr;  // MXFP4: this thread's row of E8M0 scales
-  if constexpr (WD == DT_MXFP4)
-    s_fp4 = static_cast<const uint8_t*>(wscale) + (size_t(s) * N + (bok[0] ? brow_global(brow[0]) : 0)) * (K >> 5);
+  auto brow_clamped = [&](int r) -> int { return min(brow_global(r), N - 1); };
 
-  // one K step of operands in registers: A granules, B granules, and the per-step scales
-  struct Stage {
-    uint4 a[4];
-    uint4 b[NBG];
-    float bsc;  // MXFP4: E8M0 scale of this thread's B granule
+  // ---- per-lane sources of the direct loads ---------------------------------------------------
+  // A (set up per row-block count in run()): with NS row blocks the tile's first 32*NS rows are
+  // loaded, NS instructions per wave; instruction j of wave w fills rows 8c..8c+7 (c = NS*w + j),
+  // lane -> row 8c + lane/8, slot lane%8.  Rows past the tile read a valid row and are never stored.
+  auto a_source = [&](int r) -> const uint8_t* {
+    int src = GATEUP ? 0 : m0;
+    if (r < rows) {
+      if constexpr (GATEUP) {
+        const int rr = perm[m0 + r];
+        src = (rr >= 0 && rr / k < T) ? rr / k : 0;
+      } else {
+        src = m0 + r;
+      }
+    }
+    return reinterpret_cast<const uint8_t*>(act + size_t(src) * K) + swz128(r, lane & 7) * 16;
   };
+  // B: 128-byte rows like A (bf16); 64-byte rows: c = 2w + j, lane -> row 16c + lane/4 (fp8);
+  // 32-byte rows: c = w, lane -> row 32c + lane/2 (fp4)
+  const uint8_t* bsrc[F::INSTR];
+#pragma unroll
+  for (int j = 0; j < F::INSTR; ++j) {
+    const int c = F::INSTR * wv + j;
+    int r, g;
+    if constexpr (WD == DT_BF16) {
+      r = 8 * c + (lane >> 3);
+      g = swz128(r, lane & 7);
+    } else if constexpr (WD == DT_FP8) {
+      r = 16 * c + (lane >> 2);
+      g = swz64(r, lane & 3);
+    } else {
+      r = 32 * c + (lane >> 1);
+      g = swz32(r, lane & 1);
+    }
+    bsrc[j] = wslot + size_t(brow_clamped(r)) * rb + g * 16;
+  }
+
+  // ---- per-tile side data in LDS: row validity, FP8 block scales, MXFP4 scales ------------------
+  if (tid < BM) {
+    bool ok = tid < rows;
+    if constexpr (GATEUP) {
+      if (ok) {
+        const int rr = perm[m0 + tid];
+        ok = rr >= 0 && rr / k < T;
+      }
+    }
+    rowok[tid] = ok;
+  }
   const int bl = GATEUP ? (ln < 16 ? 16 * wv + ln : 64 + 16 * wv + (ln - 16)) : 32 * wv + ln;
   constexpr bool kBlockScaled = WD == DT_FP8;
-  // FP8: the tile's B rows lie in at most three 128-row scale blocks (gate rows in one, up rows
-  // in one or two; down rows in one).  Their K-block scales are staged in LDS once per tile;
-  // lane column bl reads the row of its own weight row's block.
-  __shared__ float Ssc[3][64];
   int srow = 0;
   if constexpr (kBlockScaled) {
+    // the tile's B rows lie in at most three 128-row scale blocks
     const int KB = (K + 127) >> 7;
     const int NBk = (N + 127) >> 7;
     int blk[3];
-    blk[0] = brow_global(0) >> 7;
-    blk[1] = GATEUP ? (brow_global(64) >> 7) : blk[0];
-    blk[2] = GATEUP ? min(brow_global(127) >> 7, NBk - 1) : blk[0];
+    blk[0] = brow_clamped(0) >> 7;
+    blk[1] = GATEUP ? (brow_clamped(64) >> 7) : blk[0];
+    blk[2] = GATEUP ? (brow_clamped(127) >> 7) : blk[0];
     const float* sbase = static_cast<const float*>(wscale) + size_t(s) * NBk * KB;
     for (int t = tid; t < 3 * KB; t += kThreads) {
       const int r = t / KB, kb = t - r * KB;
-      Ssc[r][kb] = sbase[size_t(min(blk[r], NBk - 1)) * KB + kb];
+      Ssc[r][kb] = sbase[size_t(blk[r]) * KB + kb];
     }
-    const int gb = min(brow_global(bl), N - 1) >> 7;
+    const int gb = brow_clamped(bl) >> 7;
     srow = gb == blk[0] ? 0 : gb == blk[1] ? 1 : 2;
   }
-  // Loads are unconditional (rows outside the tile read a valid row and are zeroed or ignored
-  // later) so that the number of loads in flight is static and the waits stay precise.
-  auto load = [&](int kk, Stage& st) {
-    const int k0 = kk * BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (XT == DT_F32) {
-        const float4 f0 = reinterpret_cast<const float4*>(arow[i] + size_t(k0) * 4)[0];
-        const float4 f1 = reinterpret_cast<const float4*>(arow[i] + size_t(k0) * 4)[1];
-        uint4 v;
-        v.x = uint32_t(f32_to_bf16(f0.x)) | (uint32_t(f32_to_bf16(f0.y)) << 16);
-        v.y = uint32_t(f32_to_bf16(f0.z)) | (uint32_t(f32_to_bf16(f0.w)) << 16);
-        v.z = uint32_t(f32_to_bf16(f1.x)) | (uint32_t(f32_to_bf16(f1.y)) << 16);
-        v.w = uint32_t(f32_to_bf16(f1.z)) | (uint32_t(f32_to_bf16(f1.w)) << 16);
-        st.a[i] = v;
-      } else {
-        st.a[i] = *reinterpret_cast<const uint4*>(arow[i] + size_t(k0) * 2);
+  if constexpr (WD == DT_MXFP4) {
+    // E8M0 scales of the tile's 128 rows over all of K: [row][K/32] (K/32 is even: K % 64 == 0)
+    const int KB = K >> 5;
+    const uint8_t* sb = static_cast<const uint8_t*>(wscale) + size_t(s) * N * KB;
+    if (KB % 16 == 0) {
+      const int per_row = KB >> 4;
+      for (int t = tid; t < BN * per_row; t += kThreads) {
+        const int r = t / per_row, q = t - r * per_row;
+        reinterpret_cast<uint4*>(Sfp4 + r * KB)[q] = reinterpret_cast<const uint4*>(sb + size_t(brow_clamped(r)) * KB)[q];
+      }
+    } else {
+      const int per_row = KB >> 1;
+      for (int t = tid; t < BN * per_row; t += kThreads) {
+        const int r = t / per_row, q = t - r * per_row;
+        reinterpret_cast<uint16_t*>(Sfp4 + r * KB)[q] = reinterpret_cast<const uint16_t*>(sb + size_t(brow_clamped(r)) * KB)[q];
       }
     }
-#pragma unroll
-    for (int i = 0; i < NBG; ++i) {
-      const size_t byte = WD == DT_BF16 ? size_t(k0 + bcol[i]) * 2 : WD == DT_FP8 ? size_t(k0 + bcol[i]) : size_t(k0 + bcol[i]) / 2;
-      st.b[i] = ld_stream16(bsrc[i] + byte);
-    }
-    if constexpr (WD == DT_MXFP4) st.bsc = e8m0_to_f32(s_fp4[(k0 + bcol[0]) >> 5]);
-  };
-  auto store = [&](int buf, const Stage& st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t m = aok[i] ? 0xFFFFFFFFu : 0u;
-      *reinterpret_cast<uint4*>(&As[buf][((tid >> 3) + 32 * i) * kStride + (tid & 7) * 8]) =
-          make_uint4(st.a[i].x & m, st.a[i].y & m, st.a[i].z & m, st.a[i].w & m);
-    }
-#pragma unroll
-    for (int i = 0; i < NBG; ++i) {
-      uint16_t* dst = &Bs[buf][brow[i] * kStride + bcol[i]];
-      if constexpr (WD == DT_BF16) {
-        *reinterpret_cast<uint4*>(dst) = st.b[i];
-      } else if constexpr (WD == DT_FP8) {
-        uint4 a, b;
-        fp8x16_to_bf16(st.b[i], a, b);
-        reinterpret_cast<uint4*>(dst)[0] = a;
-        reinterpret_cast<uint4*>(dst)[1] = b;
-      } else {
-        uint4 o[4];
-        fp4x32_to_bf16(st.b[i], st.bsc, o);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) reinterpret_cast<uint4*>(dst)[q] = o[q];
-      }
-    }
-  };
+  }
 
-  const int nk_total = K / BK;
-  // The K loop for NS = ceil(rows / 32) row blocks (a compile-time count: straight-line MFMAs).
-  // Operands of step k+2 are loaded while step k runs; step k+1 is written to the other LDS
-  // stage after step k's MFMAs.
+  const int nk = K / BK;
+
   auto run = [&](auto ns_c) {
     constexpr int NS = decltype(ns_c)::value;
+    constexpr int kLoads = NS + F::INSTR;            // direct loads per wave and step
+    constexpr int NST = F::nstage(NS);                // K steps in flight
+    constexpr int SB = F::stage_bytes(NS);            // bytes per stage: A rows, then the B tile
+    constexpr int AB = NS * 4096;
+    static_assert(NST >= 2, "LDS budget");
+    const uint8_t* asrc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) asrc[j] = a_source(8 * (NS * wv + j) + (lane >> 3));
+    auto issue = [&](int kk, uint8_t* st) {  // direct loads of K step kk into stage st
+#pragma unroll
+      for (int j = 0; j < NS; ++j) dma16(asrc[j] + size_t(kk) * BK * 2, st + (NS * wv + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < F::INSTR; ++j) dma16(bsrc[j] + size_t(kk) * (F::ROW), st + AB + (F::INSTR * wv + j) * 1024);
+    };
+
     f32x16_t acc[NS], tmp[NS];
 #pragma unroll
     for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[ms][r] = tmp[ms][r] = 0.0f;
-    auto compute = [&](int buf) {
+
+    // B fragment of lane (column bl) for K sub-step ks of stage st
+    auto bfrag = [&](const uint8_t* st, int kk, int ks) -> bf16x8_t {
+      const uint8_t* B = st + AB;
+      if constexpr (WD == DT_BF16) {
+        return *reinterpret_cast<const bf16x8_t*>(B + bl * 128 + swz128(bl, ks * 2 + kh) * 16);
+      } else if constexpr (WD == DT_FP8) {
+        const uint2 q = *reinterpret_cast<const uint2*>(B + bl * 64 + swz64(bl, ks) * 16 + kh * 8);
+        uint32_t o[4];
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true));
+        return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+      } else {
+        const uint32_t q = *reinterpret_cast<const uint32_t*>(B + bl * 32 + swz32(bl, ks >> 1) * 16 + (ks & 1) * 8 + kh * 4);
+        const float sc = e8m0_to_f32(Sfp4[bl * (K >> 5) + kk * 2 + (ks >> 1)]);
+        uint32_t o[4];
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
+        return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+      }
+    };
+
+    // prologue: side data visible, the first NST-1 steps in flight (steps past the end re-load
+    // the last step, unused, so every wave always has the same number of loads in flight)
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p) issue(min(p, nk - 1), smem + p * SB);
+    int sr = 0;             // stage of step kk
+    int sw = NST - 1;       // stage that step kk loads into
+    for (int kk = 0; kk < nk; ++kk) {
+      // this wave's loads of step kk are done once at most the next NST-2 steps' remain;
+      // after the barrier every wave's are, and every wave has left step kk-1 (whose stage is sw)
+      wait_vmcnt<kLoads * (NST - 2)>();
+      __builtin_amdgcn_s_barrier();
+      issue(min(kk + NST - 1, nk - 1), smem + sw * SB);
+      const uint8_t* st = smem + sr * SB;
+      sr = sr + 1 == NST ? 0 : sr + 1;
+      sw = sw + 1 == NST ? 0 : sw + 1;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        const bf16x8_t bfrag = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][bl * kStride + ks * 16 + kh * 8]);
-        bf16x8_t afrag[NS];
+        const bf16x8_t b = bfrag(st, kk, ks);
+        bf16x8_t a[NS];
 #pragma unroll
-        for (int ms = 0; ms < NS; ++ms)
-          afrag[ms] = *reinterpret_cast<const bf16x8_t*>(&As[buf][(ms * 32 + ln) * kStride + ks * 16 + kh * 8]);
+        for (int ms = 0; ms < NS; ++ms) {
+          const int m = ms * 32 + ln;
+          a[ms] = *reinterpret_cast<const bf16x8_t*>(st + m * 128 + swz128(m, ks * 2 + kh) * 16);
+        }
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms) {
           if constexpr (kBlockScaled)
-            tmp[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ms], bfrag, tmp[ms], 0, 0, 0);
+            tmp[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ms], b, tmp[ms], 0, 0, 0);
           else
-            acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ms], bfrag, acc[ms], 0, 0, 0);
+            acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ms], b, acc[ms], 0, 0, 0);
         }
       }
-    };
-    // end of a 128-wide K block (or of K): fold the block's partial sums in with their scale
-    auto fold = [&](int kk) {
       if constexpr (kBlockScaled) {
-        if (((kk + 1) * BK) % 128 == 0 || kk + 1 == nk_total) {
+        // end of a 128-wide K block (or of K): fold the block's partial sums in with their scale
+        if (((kk + 1) * BK) % 128 == 0 || kk + 1 == nk) {
           const float sc = Ssc[srow][(kk * BK) >> 7];
 #pragma unroll
           for (int ms = 0; ms < NS; ++ms)
@@ -284,30 +308,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
             }
         }
       }
-    };
-    const int nk = nk_total;
-    Stage s0, s1;
-    // prefetches past the last step reload the last step (and are ignored): the number of
-    // loads in flight is the same on every path, which keeps the compiler's waits exact
-    load(0, s0);
-    load(min(1, nk - 1), s1);
-    store(0, s0);
-    __syncthreads();
-    for (int kk = 0; kk < nk; kk += 2) {
-      // step kk from LDS stage 0; s1 holds step kk+1
-      load(min(kk + 2, nk - 1), s0);
-      compute(0);
-      fold(kk);
-      if (kk + 1 < nk) store(1, s1);
-      __syncthreads();
-      if (kk + 1 >= nk) break;
-      // step kk+1 from LDS stage 1; s0 holds step kk+2
-      load(min(kk + 3, nk - 1), s1);
-      compute(1);
-      fold(kk + 1);
-      if (kk + 2 < nk) store(0, s0);
-      __syncthreads();
     }
+    wait_vmcnt<0>();  // the trailing re-loads must land before the work-group's LDS is released
 
     // ---- epilogue: accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4 of its row block,
     // column l%32
@@ -321,7 +323,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
           const float o = __shfl_xor(v, 16);
           if (ln < 16 && m < rows) {
             const int i = n0 + 16 * wv + ln;
-            if (i < I) static_cast<uint16_t*>(out)[size_t(m0 + m) * I + i] = f32_to_bf16(silu(v) * o);
+            if (i < I)
+              static_cast<uint16_t*>(out)[size_t(m0 + m) * I + i] = rowok[m] ? f32_to_bf16(silu(v) * o) : uint16_t(0);
           }
         } else {
           const int h = n0 + 32 * wv + ln;
@@ -338,8 +341,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
   }
 }
 
+// fp32 activations -> bf16 (nearest even) for the matrix-core path
+__global__ void cast_bf16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
+    y[i] = f32_to_bf16(x[i]);
+}
+
 // ---------------------------------------------------------------------------------------------
-// tile scheduler: M tiles per slot, exclusive scan, then one entry per (slot, N tile, M tile)
+// tile scheduler: M tiles per slot, exclusive scan, then one entry per (slot, M tile, N tile)
 // for both GEMMs.  Entry = {slot, (m_tile << 8) | n_tile}.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSchedThreads = 1024;
@@ -382,7 +391,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   if (tid == 0) mbase[S] = MT;
   __syncthreads();
   // entries: tile L of a GEMM with NT column tiles belongs to the last slot s with
-  // mbase[s] * NT <= L; within the slot, L - mbase[s]*NT = n_tile * mt_s + m_tile
+  // mbase[s] * NT <= L; within the slot, L - mbase[s]*NT = m_tile * NT + n_tile (the N tiles of
+  // one M tile are consecutive: co-resident blocks share the activation rows)
   for (int g = 0; g < 2; ++g) {
     const int NT = g ? nt_dn : nt_gu;
     int2* tl = g ? tiles_dn : tiles_gu;
@@ -399,7 +409,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
       const int s = lo;
       const int mt = mbase[s + 1] - mbase[s];
       const int local2 = L - mbase[s] * NT;
-      const int n = local2 / mt, m = local2 - n * mt;
+      const int m = local2 / NT, n = local2 - m * NT;
       tl[L] = make_int2(s, (m << 8) | n);
     }
   }
@@ -433,14 +443,16 @@ template <int WD>
 static hipError_t gate_up_t(const GemmArgs& g, hipStream_t st) {
   const size_t grid = gemm_tiles_max(g.T, g.k, g.S, gemm_nt_gate_up(g.I));
   if (grid == 0) return hipSuccess;
-  if (g.xdt == DT_F32)
-    gemm::gemm_kernel<WD, true, DT_F32><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-        static_cast<const uint8_t*>(g.w_gu), g.s_gu, g.x, g.perm, g.off, g.tiles_gu, g.counts, g.T, g.k, g.H,
-        2 * g.I, g.I, g.a);
-  else
-    gemm::gemm_kernel<WD, true, DT_BF16><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-        static_cast<const uint8_t*>(g.w_gu), g.s_gu, g.x, g.perm, g.off, g.tiles_gu, g.counts, g.T, g.k, g.H,
-        2 * g.I, g.I, g.a);
+  const void* x = g.x;
+  if (g.xdt == DT_F32) {  // the matrix cores read bf16: round the activations once
+    const size_t n = size_t(g.T) * g.H;
+    gemm::cast_bf16_kernel<<<dim3(unsigned((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256), 0, st>>>(
+        static_cast<const float*>(g.x), static_cast<uint16_t*>(g.xb), n);
+    x = g.xb;
+  }
+  gemm::gemm_kernel<WD, true><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
+      static_cast<const uint8_t*>(g.w_gu), g.s_gu, static_cast<const uint16_t*>(x), g.perm, g.off, g.tiles_gu,
+      g.counts, g.T, g.k, g.H, 2 * g.I, g.I, g.a);
   return hipGetLastError();
 }
 
@@ -449,7 +461,7 @@ static hipError_t down_t(const GemmArgs& g, hipStream_t st) {
   const size_t grid = gemm_tiles_max(g.T, g.k, g.S, gemm_nt_down(g.H));
   if (grid == 0) return hipSuccess;
   gemm::gemm_kernel<WD, false><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-      static_cast<const uint8_t*>(g.w_d), g.s_d, g.a, nullptr, g.off, g.tiles_dn,
+      static_cast<const uint8_t*>(g.w_d), g.s_d, static_cast<const uint16_t*>(g.a), nullptr, g.off, g.tiles_dn,
       g.counts + 1, g.T, g.k, g.I, g.H, g.I, g.y);
   return hipGetLastError();
 }

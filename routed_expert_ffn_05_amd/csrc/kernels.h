@@ -49,7 +49,8 @@ struct GemmArgs {
   const void* s_gu;
   const void* w_d;
   const void* s_d;
-  const void* x;        // [T, H] bf16 (or fp32, rounded to bf16 when staged)
+  const void* x;        // [T, H] bf16 or fp32
+  void* xb;             // [T, H] bf16 scratch: fp32 activations rounded once for the matrix cores
   const int32_t* perm;
   const int32_t* off;
   void* a;              // [T*k, I] bf16

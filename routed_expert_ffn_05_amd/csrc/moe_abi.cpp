@@ -93,9 +93,12 @@ int check_weights(const moe_weights* w) {
   return MOE_OK;
 }
 
-// the matrix-core path needs bf16-exact weights and K-steps of 64
+// the matrix-core path needs bf16-exact weights, K steps of 64 and (MXFP4) the per-row E8M0
+// scales of K <= 4096 staged in LDS
 bool gemm_capable(const moe_weights* w) {
-  return w->wdtype != MOE_F32 && w->H % 64 == 0 && w->I % 64 == 0;
+  if (w->wdtype == MOE_F32 || w->H % 64 || w->I % 64) return false;
+  if (w->wdtype == MOE_MXFP4 && (w->H > 4096 || w->I > 4096)) return false;
+  return true;
 }
 
 // AUTO: the GEMM path once slots hold several rows on average (measured crossover: the GEMV
@@ -111,7 +114,8 @@ int check_path_mode(int path, int mode, const moe_weights* w) {
     return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
   if (mode != MOE_MODE_A && mode != MOE_MODE_B) return fail(MOE_ERR_INVALID_ARG, "unknown mode %d", mode);
   if (path == MOE_PATH_GEMM && !gemm_capable(w))
-    return fail(MOE_ERR_UNSUPPORTED, "the GEMM path needs bf16, FP8 or MXFP4 weights and H, I multiples of 64");
+    return fail(MOE_ERR_UNSUPPORTED, "the GEMM path needs bf16, FP8 or MXFP4 weights, H and I multiples of 64 "
+                                     "(and at most 4096 for MXFP4)");
   if (mode == MOE_MODE_B) return fail(MOE_ERR_UNSUPPORTED, "mode B is not available in this build");
   return MOE_OK;
 }
@@ -132,6 +136,7 @@ struct Carve {
 // expert-FFN workspace: [256: header][a: T*k*I fp32 (GEMV) or bf16 (GEMM)][tile lists][counts]
 struct FfnWs {
   void* a;
+  void* xb;
   int2* tiles_gu;
   int2* tiles_dn;
   int32_t* counts;
@@ -142,6 +147,7 @@ FfnWs carve_ffn(void* ws, const moe_weights* w, int T, int k) {
   FfnWs f{};
   c.take<char>(256);
   f.a = c.take<char>(size_t(T) * k * w->I * sizeof(float));
+  f.xb = c.take<char>(size_t(T) * w->H * 2);
   f.tiles_gu = c.take<int2>(moe::gemm_tiles_max(T, k, w->S, moe::gemm_nt_gate_up(w->I)) * sizeof(int2));
   f.tiles_dn = c.take<int2>(moe::gemm_tiles_max(T, k, w->S, moe::gemm_nt_down(w->H)) * sizeof(int2));
   f.counts = c.take<int32_t>(2 * sizeof(int32_t));
@@ -317,6 +323,7 @@ moe::GemmArgs gemm_args(const moe_weights* w, const void* x, int x_dtype, int T,
   g.perm = perm;
   g.off = off;
   g.a = f.a;
+  g.xb = f.xb;
   g.y = y;
   g.tiles_gu = f.tiles_gu;
   g.tiles_dn = f.tiles_dn;

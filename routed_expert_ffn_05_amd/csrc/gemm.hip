@@ -3,22 +3,23 @@
 //   gate/up:  a[p, i] = silu(x_p . W_g[s,i,:]) * (x_p . W_u[s,i,:])  for the rows p of slot s
 //   down:     y[p, h] = a_p . W_d[s,h,:]
 //
-// Tiles.  A work-group computes a BM x BN output tile of one slot with 4 waves side by side along
-// N (32 columns each) and up to 4 MFMA row blocks of 32 rows; a tile whose slot has fewer rows
+// Tiles.  A work-group (8 waves) computes a BM x BN output tile of one slot: each wave owns 32 of
+// the BN = 256 columns and up to 4 MFMA row blocks of 32 rows; a tile whose slot has fewer rows
 // runs only ceil(rows/32) row blocks, so a slot of n rows costs that much matrix work while its
-// weights are streamed once per 128-row M tile.
+// weights are streamed once per 128-row M tile.  The wide N tile halves how often each activation
+// row is moved from L2 into LDS (the on-chip traffic that bounds these GEMMs).
 // Staging.  Operand tiles of each K step (BK = 64) move from HBM to LDS by direct LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane) with no register
-// staging; one explicit vmcnt wait and one barrier per step.  A stage holds the A rows the tile
-// uses plus the B tile, so tiles with fewer row blocks keep more K steps in flight within the same
-// LDS budget (2 to 6 stages).  Within a row, the
-// 16-byte granule g of row r is stored at slot g ^ f(r) (f spreads 16 consecutive rows over
-// distinct bank groups for the MFMA fragment reads).  Weights stay in their stored format in LDS
-// and are decoded when a B fragment is read: e4m3fn -> bf16 is exact; e2m1 times a power-of-two
-// E8M0 scale -> bf16 is exact (the conversion applies the scale).
+// staging; one explicit vmcnt wait and one barrier per step, the loads of a step spread over its
+// MFMA sub-steps.  One work-group per CU owns most of the LDS: a stage holds the A rows the tile
+// uses plus the B tile, and tiles with fewer row blocks keep more K steps in flight (3 to 8).
+// Within a row, the 16-byte granule g of row r is stored at slot g ^ f(r) (f spreads consecutive
+// rows over distinct bank groups for the MFMA fragment reads).  Weights stay in their stored
+// format in LDS and are decoded when a B fragment is read: e4m3fn -> bf16 is exact; e2m1 times a
+// power-of-two E8M0 scale -> bf16 is exact (the conversion applies the scale).
 // FP8 block scales.  A 128x128 block scale is constant over a lane's column and a 128-wide K
 // block: each lane accumulates a K block in a temporary and adds scale * temporary to the result.
-// Gate/up fusion.  The N tile holds 64 gate rows then the 64 matching up rows; wave w reads its
+// Gate/up fusion.  The N tile holds 128 gate rows then the 128 matching up rows; wave w reads its
 // 32 MFMA columns as gate rows 16w..16w+15 followed by up rows 16w..16w+15, so lanes l and l+16
 // hold gate and up of the same (row, i) and SiLU(g)*u is formed in registers.
 // Scheduling.  A one-work-group kernel lists the tiles in (slot, M tile, N tile) order; blocks are
@@ -33,24 +34,25 @@
 namespace moe {
 namespace gemm {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kThreads = 256;
+constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kMaxFp4Kb = 128;  // MXFP4: E8M0 scales per row staged in LDS (K <= 4096)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const void lds_void;
 
-// B operand bytes per row and K step, stages in flight
+// B operand bytes per row and K step, direct loads per wave and step, LDS for the stages
 template <int WD> struct BFmt {
   static constexpr int ROW = WD == DT_BF16 ? 128 : WD == DT_FP8 ? 64 : 32;
   static constexpr int STAGE = BN * ROW;
-  static constexpr int INSTR = STAGE / 4096;  // 1 KiB direct loads per wave and step
-  // LDS for the stages (two work-groups per CU with the format's other LDS data)
-  static constexpr int BUDGET = WD == DT_BF16 ? 64 * 1024 : WD == DT_FP8 ? 72 * 1024 : 60 * 1024;
+  static constexpr int INSTR = STAGE / (1024 * kWaves);
+  // the MXFP4 tile keeps its E8M0 scales (BN x K/32 bytes) in LDS beside the stages
+  static constexpr int BUDGET = WD == DT_MXFP4 ? 112 * 1024 : 144 * 1024;
   // a K step of a tile with NS row blocks occupies NS*4 KiB of A plus the B tile; as many steps
-  // are kept in flight as the budget holds (at most 6)
+  // are kept in flight as the budget holds (at most 8)
   static constexpr int stage_bytes(int ns) { return ns * 4096 + STAGE; }
-  static constexpr int nstage(int ns) { return BUDGET / stage_bytes(ns) < 6 ? BUDGET / stage_bytes(ns) : 6; }
+  static constexpr int nstage(int ns) { return BUDGET / stage_bytes(ns) < 8 ? BUDGET / stage_bytes(ns) : 8; }
 };
 
 __device__ __forceinline__ int xcd_remap(int b, int n) {
@@ -60,13 +62,18 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return base + j;
 }
 
-// 16 bytes per lane from `src` into LDS at (wave-uniform) lds + 16*lane.  Written as inline
-// assembly so that the compiler's wait insertion does not treat it as aliasing every LDS read:
-// the kernel orders these loads itself (explicit vmcnt waits and barriers), and no other vector
-// memory load is in flight while they are.
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(uint32_t(size_t((lds_void*)lds)));
+// 16 bytes per lane from `src` into LDS at byte address lds + 16*lane (lds wave-uniform).
+// Written as inline assembly so that the compiler's wait insertion does not treat it as aliasing
+// every LDS read: the kernel orders these loads itself (explicit vmcnt waits and barriers), and no
+// other vector memory load is in flight while they are.  The memory clobber keeps LDS reads from
+// moving across it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(uint32_t(size_t((lds_void*)p)));
 }
 
 // swizzled position of 16-byte granule g in a row r of a 128-byte (bf16) tile row
@@ -89,20 +96,18 @@ __host__ __device__ constexpr size_t row_bytes(int K) {
   return WD == DT_BF16 ? size_t(K) * 2 : WD == DT_FP8 ? size_t(K) : size_t(K) / 2;
 }
 
-constexpr int kMaxFp4Kb = 128;  // MXFP4: E8M0 scales per row staged in LDS (K <= 4096)
-
 // ---------------------------------------------------------------------------------------------
 // GATEUP = true:  A = x rows (through perm), B = W_gu[s] (gate/up interleaved), out a (bf16)
 // GATEUP = false: A = a rows (positions),    B = W_d[s],                        out y (fp32)
 // ---------------------------------------------------------------------------------------------
 template <int WD, bool GATEUP>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ off, const int2* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, int T, int k, int K, int N, int I, void* __restrict__ out) {
   using F = BFmt<WD>;
   __shared__ __align__(16) uint8_t smem[F::BUDGET];
-  __shared__ float Ssc[3][64];                                    // FP8 block scales
+  __shared__ float Ssc[4][64];                                    // FP8 block scales
   __shared__ __align__(16) uint8_t Sfp4[WD == DT_MXFP4 ? BN * kMaxFp4Kb : 16];  // MXFP4 scales
   __shared__ uint8_t rowok[BM];
   const int n_act = ntiles[0];
@@ -115,22 +120,23 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
   const int rows = min(BM, hi - m0);
   if (rows <= 0) return;
   const int nsub = (rows + 31) >> 5;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, kh = lane >> 5;
-  // output columns of this tile: gate/up -> i in [n0, n0+64); down -> h in [n0, n0+128)
+  // output columns of this tile: gate/up -> i in [n0, n0+128); down -> h in [n0, n0+256)
   const int n0 = GATEUP ? nt * (BN / 2) : nt * BN;
   const size_t rb = row_bytes<WD>(K);
   const uint8_t* wslot = w + size_t(s) * N * rb;
   auto brow_global = [&](int r) -> int {
-    if constexpr (GATEUP) return r < 64 ? n0 + r : I + n0 + (r - 64);
+    if constexpr (GATEUP) return r < BN / 2 ? n0 + r : I + n0 + (r - BN / 2);
     return n0 + r;
   };
+  // rows past N read the last row (valid memory; their columns are never stored)
   auto brow_clamped = [&](int r) -> int { return min(brow_global(r), N - 1); };
 
   // ---- per-lane sources of the direct loads ---------------------------------------------------
   // A (set up per row-block count in run()): with NS row blocks the tile's first 32*NS rows are
-  // loaded, NS instructions per wave; instruction j of wave w fills rows 8c..8c+7 (c = NS*w + j),
-  // lane -> row 8c + lane/8, slot lane%8.  Rows past the tile read a valid row and are never stored.
+  // loaded as 4*NS chunks of 8 rows x 128 bytes; chunk c is issued by wave c % 8, lane -> row
+  // 8c + lane/8, slot lane%8.  Rows past the tile read a valid row and are never stored.
   auto a_source = [&](int r) -> const uint8_t* {
     int src = GATEUP ? 0 : m0;
     if (r < rows) {
@@ -143,8 +149,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     }
     return reinterpret_cast<const uint8_t*>(act + size_t(src) * K) + swz128(r, lane & 7) * 16;
   };
-  // B: 128-byte rows like A (bf16); 64-byte rows: c = 2w + j, lane -> row 16c + lane/4 (fp8);
-  // 32-byte rows: c = w, lane -> row 32c + lane/2 (fp4)
+  // B: chunk c = INSTR*w + j covers 1 KiB of the tile: 128-byte rows like A (bf16); 64-byte rows:
+  // lane -> row 16c + lane/4 (fp8); 32-byte rows: lane -> row 32c + lane/2 (fp4)
   const uint8_t* bsrc[F::INSTR];
 #pragma unroll
   for (int j = 0; j < F::INSTR; ++j) {
@@ -174,61 +180,91 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     }
     rowok[tid] = ok;
   }
-  const int bl = GATEUP ? (ln < 16 ? 16 * wv + ln : 64 + 16 * wv + (ln - 16)) : 32 * wv + ln;
+  // B column of this lane (a row of the weight tile)
+  const int bl = GATEUP ? (ln < 16 ? 16 * wv + ln : BN / 2 + 16 * wv + (ln - 16)) : 32 * wv + ln;
   constexpr bool kBlockScaled = WD == DT_FP8;
   int srow = 0;
   if constexpr (kBlockScaled) {
-    // the tile's B rows lie in at most three 128-row scale blocks
+    // the tile's B rows lie in at most four 128-row scale blocks: those of tile rows 0, 127, 128
+    // and 255 (gate/up: the gate rows start on a block boundary, the up rows may straddle one)
     const int KB = (K + 127) >> 7;
     const int NBk = (N + 127) >> 7;
-    int blk[3];
+    int blk[4];
     blk[0] = brow_clamped(0) >> 7;
-    blk[1] = GATEUP ? (brow_clamped(64) >> 7) : blk[0];
-    blk[2] = GATEUP ? (brow_clamped(127) >> 7) : blk[0];
+    blk[1] = brow_clamped(127) >> 7;
+    blk[2] = brow_clamped(128) >> 7;
+    blk[3] = brow_clamped(255) >> 7;
     const float* sbase = static_cast<const float*>(wscale) + size_t(s) * NBk * KB;
-    for (int t = tid; t < 3 * KB; t += kThreads) {
+    for (int t = tid; t < 4 * KB; t += kThreads) {
       const int r = t / KB, kb = t - r * KB;
       Ssc[r][kb] = sbase[size_t(blk[r]) * KB + kb];
     }
     const int gb = brow_clamped(bl) >> 7;
-    srow = gb == blk[0] ? 0 : gb == blk[1] ? 1 : 2;
+    srow = gb == blk[0] ? 0 : gb == blk[1] ? 1 : gb == blk[2] ? 2 : 3;
   }
+  // MXFP4: E8M0 scales of the tile's rows over all of K, [row][K/32] in LDS (K/32 is even).
+  // With K % 512 == 0 a row is gpr whole 16-byte granules, stored rotated by a per-row key so that
+  // the rows read together by one instruction fall in different LDS banks (granule q of row r at
+  // slot (q + key(r)) % gpr); they arrive by direct loads issued with the first stages.  Otherwise
+  // the work-group copies them unrotated before the main loop.
+  const int KB32 = K >> 5;
+  const uint8_t* fp4_src = WD == DT_MXFP4 ? static_cast<const uint8_t*>(wscale) + size_t(s) * N * KB32 : nullptr;
+  const bool fp4_async = WD == DT_MXFP4 && KB32 % 16 == 0;
+  const int gpr = fp4_async ? KB32 >> 4 : 1;
+  // rows r and r + D start in the same bank: D = 64 dwords over the row's dwords, made coprime
+  const int fp4_d = fp4_async ? 16 / (gpr & -gpr < 16 ? gpr & -gpr : 16) : 1;
+  auto fp4_key = [&](int r) -> int { return fp4_async ? (r / fp4_d) % gpr : 0; };
   if constexpr (WD == DT_MXFP4) {
-    // E8M0 scales of the tile's 128 rows over all of K: [row][K/32] (K/32 is even: K % 64 == 0)
-    const int KB = K >> 5;
-    const uint8_t* sb = static_cast<const uint8_t*>(wscale) + size_t(s) * N * KB;
-    if (KB % 16 == 0) {
-      const int per_row = KB >> 4;
+    if (!fp4_async) {
+      const int per_row = KB32 >> 1;
       for (int t = tid; t < BN * per_row; t += kThreads) {
         const int r = t / per_row, q = t - r * per_row;
-        reinterpret_cast<uint4*>(Sfp4 + r * KB)[q] = reinterpret_cast<const uint4*>(sb + size_t(brow_clamped(r)) * KB)[q];
-      }
-    } else {
-      const int per_row = KB >> 1;
-      for (int t = tid; t < BN * per_row; t += kThreads) {
-        const int r = t / per_row, q = t - r * per_row;
-        reinterpret_cast<uint16_t*>(Sfp4 + r * KB)[q] = reinterpret_cast<const uint16_t*>(sb + size_t(brow_clamped(r)) * KB)[q];
+        reinterpret_cast<uint16_t*>(Sfp4 + r * KB32)[q] = reinterpret_cast<const uint16_t*>(fp4_src + size_t(brow_clamped(r)) * KB32)[q];
       }
     }
   }
+  const int fp4_row = bl * KB32, fp4_keyl = fp4_key(bl);
 
   const int nk = K / BK;
 
   auto run = [&](auto ns_c) {
     constexpr int NS = decltype(ns_c)::value;
-    constexpr int kLoads = NS + F::INSTR;            // direct loads per wave and step
+    constexpr int NA = 4 * NS;                        // A chunks per step
+    constexpr int A_HI = (NA + kWaves - 1) / kWaves;  // A chunks of waves 0 .. NA%8-1 (or all)
+    constexpr int A_LO = NA / kWaves;                 // A chunks of the other waves
     constexpr int NST = F::nstage(NS);                // K steps in flight
     constexpr int SB = F::stage_bytes(NS);            // bytes per stage: A rows, then the B tile
     constexpr int AB = NS * 4096;
-    static_assert(NST >= 2, "LDS budget");
-    const uint8_t* asrc[NS];
+    constexpr int KS = BK / 16;                       // MFMA K sub-steps per step
+    constexpr int kReads = NS + (WD == DT_MXFP4 ? 2 : 1);  // LDS reads per sub-step
+    static_assert(NST >= 3, "LDS budget");
+    const int na = (NA % kWaves == 0 || wv < NA % kWaves) ? A_HI : A_LO;  // this wave's A chunks
+    const int nl = na + F::INSTR;                                       // its loads per step
+    const uint8_t* asrc[A_HI];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) asrc[j] = a_source(8 * (NS * wv + j) + (lane >> 3));
-    auto issue = [&](int kk, uint8_t* st) {  // direct loads of K step kk into stage st
+    for (int j = 0; j < A_HI; ++j) {
+      const int c = j < na ? wv + kWaves * j : wv;  // unused entries point at a valid row
+      asrc[j] = a_source(8 * c + (lane >> 3));
+    }
+    const uint32_t lds0 = lds_addr(smem);
+    // direct load j of this wave for K step kk into the stage at LDS address st: j < na are
+    // A chunks, the rest B
+    auto issue_one = [&](int j, int kk, uint32_t st) {
+      if (j < na) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) dma16(asrc[j] + size_t(kk) * BK * 2, st + (NS * wv + j) * 1024);
+        for (int q = 0; q < A_HI; ++q)
+          if (q == j) dma16(asrc[q] + size_t(kk) * BK * 2, st + (wv + kWaves * q) * 1024);
+      } else {
 #pragma unroll
-      for (int j = 0; j < F::INSTR; ++j) dma16(bsrc[j] + size_t(kk) * (F::ROW), st + AB + (F::INSTR * wv + j) * 1024);
+        for (int q = 0; q < F::INSTR; ++q)
+          if (q == j - na) dma16(bsrc[q] + size_t(kk) * (F::ROW), st + AB + (F::INSTR * wv + q) * 1024);
+      }
+    };
+    // the step's loads are spread over its K sub-steps: group g issues loads [lo(g), lo(g+1))
+    auto issue_group = [&](int g, int kk, uint32_t st) {
+#pragma unroll
+      for (int j = 0; j < A_HI + F::INSTR; ++j)
+        if (j < nl && j >= (nl * g) / KS && j < (nl * (g + 1)) / KS) issue_one(j, kk, st);
     };
 
     f32x16_t acc[NS], tmp[NS];
@@ -237,63 +273,109 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[ms][r] = tmp[ms][r] = 0.0f;
 
-    // B fragment of lane (column bl) for K sub-step ks of stage st
-    auto bfrag = [&](const uint8_t* st, int kk, int ks) -> bf16x8_t {
+    // raw LDS fragments of one K sub-step: A rows as bf16, B in its stored format (+ MXFP4 scale)
+    struct Raw {
+      bf16x8_t a[NS];
+      uint32_t b[WD == DT_BF16 ? 4 : WD == DT_FP8 ? 2 : 1];
+      uint32_t sc;
+    };
+    auto load_raw = [&](const uint8_t* st, int kk, int ks, Raw& f) {
+#pragma unroll
+      for (int ms = 0; ms < NS; ++ms) {
+        const int m = ms * 32 + ln;
+        f.a[ms] = *reinterpret_cast<const bf16x8_t*>(st + m * 128 + swz128(m, ks * 2 + kh) * 16);
+      }
       const uint8_t* B = st + AB;
       if constexpr (WD == DT_BF16) {
-        return *reinterpret_cast<const bf16x8_t*>(B + bl * 128 + swz128(bl, ks * 2 + kh) * 16);
+        const uint4 q = *reinterpret_cast<const uint4*>(B + bl * 128 + swz128(bl, ks * 2 + kh) * 16);
+        f.b[0] = q.x; f.b[1] = q.y; f.b[2] = q.z; f.b[3] = q.w;
       } else if constexpr (WD == DT_FP8) {
         const uint2 q = *reinterpret_cast<const uint2*>(B + bl * 64 + swz64(bl, ks) * 16 + kh * 8);
-        uint32_t o[4];
-        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false));
-        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true));
-        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false));
-        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true));
-        return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        f.b[0] = q.x; f.b[1] = q.y;
       } else {
-        const uint32_t q = *reinterpret_cast<const uint32_t*>(B + bl * 32 + swz32(bl, ks >> 1) * 16 + (ks & 1) * 8 + kh * 4);
-        const float sc = e8m0_to_f32(Sfp4[bl * (K >> 5) + kk * 2 + (ks >> 1)]);
-        uint32_t o[4];
-        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
-        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
-        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
-        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
-        return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        f.b[0] = *reinterpret_cast<const uint32_t*>(B + bl * 32 + swz32(bl, ks >> 1) * 16 + (ks & 1) * 8 + kh * 4);
+        const int kb = kk * 2 + (ks >> 1);
+        if (fp4_async) {
+          int slot = (kb >> 4) + fp4_keyl;
+          slot -= slot >= gpr ? gpr : 0;
+          f.sc = Sfp4[fp4_row + slot * 16 + (kb & 15)];
+        } else {
+          f.sc = Sfp4[fp4_row + kb];
+        }
       }
     };
+    // B fragment as bf16 (e4m3fn -> bf16 exact; e2m1 x power-of-two scale -> bf16 exact)
+    auto decode_b = [&](const Raw& f) -> bf16x8_t {
+      uint32_t o[4];
+      if constexpr (WD == DT_BF16) {
+        o[0] = f.b[0]; o[1] = f.b[1]; o[2] = f.b[2]; o[3] = f.b[3];
+      } else if constexpr (WD == DT_FP8) {
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[0], 1.0f, false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[0], 1.0f, true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[1], 1.0f, false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[1], 1.0f, true));
+      } else {
+        const float sc = e8m0_to_f32(f.sc);
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[0], sc, 0));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[0], sc, 1));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[0], sc, 2));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[0], sc, 3));
+      }
+      return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+    };
 
-    // prologue: side data visible, the first NST-1 steps in flight (steps past the end re-load
-    // the last step, unused, so every wave always has the same number of loads in flight)
-    __syncthreads();
+    // prologue: side data visible (LDS writes done, then a barrier: no wait for the direct loads),
+    // the MXFP4 scales and the first NST-1 steps in flight (steps past the end re-load the last
+    // step, unused, so every wave always has the same number of loads in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (WD == DT_MXFP4) {
+      if (fp4_async) {
+        const int total = BN * gpr;  // granules, a multiple of 256
+        const uint32_t sl = lds_addr(Sfp4);
+        for (int c = wv; c * 64 < total; c += kWaves) {
+          const int L = c * 64 + lane;
+          const int r = L / gpr, slot = L - r * gpr;
+          int q = slot - fp4_key(r);
+          q += q < 0 ? gpr : 0;
+          dma16(fp4_src + size_t(brow_clamped(r)) * KB32 + q * 16, sl + c * 1024);
+        }
+      }
+    }
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p) issue(min(p, nk - 1), smem + p * SB);
+    for (int p = 0; p < NST - 1; ++p)
+#pragma unroll
+      for (int g = 0; g < KS; ++g) issue_group(g, min(p, nk - 1), lds0 + p * SB);
     int sr = 0;             // stage of step kk
     int sw = NST - 1;       // stage that step kk loads into
     for (int kk = 0; kk < nk; ++kk) {
       // this wave's loads of step kk are done once at most the next NST-2 steps' remain;
       // after the barrier every wave's are, and every wave has left step kk-1 (whose stage is sw)
-      wait_vmcnt<kLoads * (NST - 2)>();
+      if (na == A_HI) wait_vmcnt<(A_HI + F::INSTR) * (NST - 2)>();
+      else wait_vmcnt<(A_LO + F::INSTR) * (NST - 2)>();
       __builtin_amdgcn_s_barrier();
-      issue(min(kk + NST - 1, nk - 1), smem + sw * SB);
       const uint8_t* st = smem + sr * SB;
+      const uint32_t wst = lds0 + sw * SB;
+      const int kn = min(kk + NST - 1, nk - 1);
       sr = sr + 1 == NST ? 0 : sr + 1;
       sw = sw + 1 == NST ? 0 : sw + 1;
+      Raw f[2];
+      load_raw(st, kk, 0, f[0]);
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const bf16x8_t b = bfrag(st, kk, ks);
-        bf16x8_t a[NS];
-#pragma unroll
-        for (int ms = 0; ms < NS; ++ms) {
-          const int m = ms * 32 + ln;
-          a[ms] = *reinterpret_cast<const bf16x8_t*>(st + m * 128 + swz128(m, ks * 2 + kh) * 16);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) load_raw(st, kk, ks + 1, f[(ks + 1) & 1]);
+        issue_group(ks, kn, wst);
+        const bf16x8_t b = decode_b(f[ks & 1]);
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms) {
           if constexpr (kBlockScaled)
-            tmp[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ms], b, tmp[ms], 0, 0, 0);
+            tmp[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].a[ms], b, tmp[ms], 0, 0, 0);
           else
-            acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ms], b, acc[ms], 0, 0, 0);
+            acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].a[ms], b, acc[ms], 0, 0, 0);
         }
+        // keep the next sub-step's LDS reads ahead of this sub-step's matrix instructions
+        if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
       }
       if constexpr (kBlockScaled) {
         // end of a 128-wide K block (or of K): fold the block's partial sums in with their scale

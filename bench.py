@@ -274,6 +274,7 @@ def run(args):
     for i in range(args.steps):
         step(i, evs[i])
     end.record(stream)
+    host = time.perf_counter() - wall0
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
@@ -283,7 +284,8 @@ def run(args):
     gu_bytes = [gate_up_bytes(i % len(rot)) for i in range(args.steps)]
     achieved = sum(gu_bytes) / (sum(gu_ms) / 1e3) / 1e9
     layer_gbs = sum(layer_bytes(i % len(rot)) for i in range(args.steps)) / (total_ms / 1e3) / 1e9
-    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step), "
+    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host enqueue {host * 1e6 / args.steps:.1f} us/step, "
+        f"wall {wall * 1e6 / args.steps:.1f} us/step), "
         f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s; "
         f"path {'gemm' if gemm else 'gemv'}")
 

@@ -127,7 +127,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   {                                                                               \
     const float ov = __int_as_float(dpp_src_or<CTRL, RM>(NEG, __float_as_int(v))); \
     const int oi = dpp_src_or<CTRL, RM>(BIG, i);                                  \
-    const bool take = ov > v || (ov == v && oi < i);                              \
+    const bool take = (ov > v) | ((ov == v) & (oi < i));                          \
     v = take ? ov : v;                                                            \
     i = take ? oi : i;                                                            \
   }

@@ -16,7 +16,9 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, i
                           const int32_t* slot_map, int S, int32_t* counts, int32_t* slot_offsets,
                           int32_t* perm, int32_t* inv_perm, int32_t* miss_count,
                           int32_t* miss_token, int32_t* miss_expert, float* miss_weight,
-                          uint32_t* err, hipStream_t st);
+                          uint32_t* err, int32_t* scratch, hipStream_t st);
+// device scratch (bytes) launch_permute needs for T*k rows: 0 when one work-group does it all
+size_t permute_scratch_bytes(int T, int k, int E, int S);
 // top-k of every token and the permutation in one work-group (small batches)
 size_t route_permute_lds_bytes(int T, int k, int E, int S);
 hipError_t launch_route_permute(const float* logits, const float* bias, int T, int k, int E,

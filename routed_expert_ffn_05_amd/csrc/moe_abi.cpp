@@ -225,8 +225,9 @@ int moe_route(const void* x, int x_dtype, int T, int H, const float* w_router, c
 
 // ---------------------------------------------------------------------------------------------
 size_t moe_permute_workspace_size(int T, const moe_routing* cfg, int S) {
-  (void)T; (void)cfg; (void)S;
-  return 256;
+  // error word, then the per-group count table of large batches
+  if (!cfg || T < 0 || cfg->E < 1 || cfg->k < 1 || S < 1) return 256;
+  return 256 + align256(moe::permute_scratch_bytes(T, cfg->k, cfg->E, S));
 }
 
 int moe_permute(const int32_t* topk_idx, const float* topk_w, int T, const moe_routing* cfg,
@@ -252,7 +253,8 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, int T, const moe_r
   // T = 0 still writes zero counts/offsets (one small launch)
   hipError_t e = moe::launch_permute(topk_idx, topk_w, T, cfg->k, cfg->E, slot_map, S, counts,
                                      slot_offsets, perm, inv_perm, miss_count, miss_token,
-                                     miss_expert, miss_weight, static_cast<uint32_t*>(ws), st);
+                                     miss_expert, miss_weight, static_cast<uint32_t*>(ws),
+                                     reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 256), st);
   if (e != hipSuccess) return hip_fail(e, "permute");
   return MOE_OK;
 }
@@ -397,8 +399,10 @@ int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_
 
 // ---------------------------------------------------------------------------------------------
 size_t moe_route_permute_workspace_size(int T, const moe_routing* cfg, int S, int with_router_weights) {
-  (void)S;
-  return 256 + moe_route_workspace_size(T, cfg, with_router_weights);
+  // error word, router logits, then the permutation's count table
+  const size_t perm = (!cfg || T < 0 || cfg->E < 1 || cfg->k < 1 || S < 1)
+                          ? 0 : align256(moe::permute_scratch_bytes(T, cfg->k, cfg->E, S));
+  return 256 + moe_route_workspace_size(T, cfg, with_router_weights) + perm;
 }
 
 int moe_route_permute(const void* x, int x_dtype, int T, int H, const float* w_router,
@@ -451,8 +455,10 @@ int moe_route_permute(const void* x, int x_dtype, int T, int H, const float* w_r
     e = moe::launch_topk(lg, tb, tb ? 1 : 0, T, cfg->E, cfg->k, cfg->score, cfg->renorm, topk_idx, topk_w, st);
     if (e != hipSuccess) return hip_fail(e, "top-k");
   }
+  int32_t* ptab = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 256 +
+                                             moe_route_workspace_size(T, cfg, w_router != nullptr));
   e = moe::launch_permute(topk_idx, topk_w, T, cfg->k, cfg->E, slot_map, S, counts, slot_offsets, perm,
-                          inv_perm, miss_count, miss_token, miss_expert, miss_weight, err, st);
+                          inv_perm, miss_count, miss_token, miss_expert, miss_weight, err, ptab, st);
   if (e != hipSuccess) return hip_fail(e, "permute");
   return MOE_OK;
 }

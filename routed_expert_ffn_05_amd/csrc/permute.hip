@@ -12,6 +12,12 @@
 //
 // For small batches the top-k of every token runs in the same work-group first (one wave per
 // token), its results kept in LDS, so routing and permutation cost one launch.
+//
+// Large batches (more than kPermOneGroupRows rows) spread the same three steps over work-groups
+// of 1024 rows each: (1) every group counts its rows per key and per expert into a global table,
+// (2) one group sums the table, scans the slot totals and turns each group's counts into its base
+// position per key (groups in row order), (3) every group ranks its rows as in the one-group
+// version, starting from those bases.  The result is identical to the one-group version.
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -20,10 +26,58 @@ namespace moe {
 
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
+constexpr int kPermOneGroupRows = 2048;  // larger batches use the multi-group kernels
 
 // LDS words used by permute_body
 __host__ __device__ inline size_t permute_lds_words(int E, int S) {
   return size_t(kPermWaves) * (S + 1) + E + (S + 2);
+}
+
+// key of a row: slot, S for a miss, -1 for an invalid row (expert or slot out of range)
+__device__ __forceinline__ int row_key(const int32_t* topk_idx, int E, const int32_t* __restrict__ slot_map,
+                                       int S, int r, int& e) {
+  e = topk_idx[r];
+  if (e < 0 || e >= E) return -1;
+  const int s = slot_map ? slot_map[e] : e;
+  if (s < -1 || s >= S) return -1;
+  return s < 0 ? S : s;
+}
+
+// Stable scatter of rows [c0, c0+64) of one wave given its per-key running bases wbase[key]
+// (advanced past the chunk's rows): rows sharing a key are ranked by lane order.
+__device__ __forceinline__ void scatter_chunk(const int32_t* topk_idx, const float* topk_w, int k, int E,
+                                              const int32_t* __restrict__ slot_map, int S, int c0, int r1,
+                                              int32_t* wbase, int32_t* __restrict__ perm,
+                                              int32_t* __restrict__ inv_perm, int32_t* __restrict__ miss_token,
+                                              int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight) {
+  const int lane = threadIdx.x & 63;
+  const int r = c0 + lane;
+  int e = 0, key = -1;
+  if (r < r1) key = row_key(topk_idx, E, slot_map, S, r, e);
+  unsigned long long todo = __ballot(key >= 0);
+  int pos = -1;
+  while (todo) {
+    const int leader = __ffsll((long long)todo) - 1;
+    const int lkey = __shfl(key, leader);
+    const unsigned long long m = __ballot(key == lkey);
+    const int b = wbase[lkey];
+    if (key == lkey) pos = b + __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == leader) wbase[lkey] = b + __popcll(m);
+    todo &= ~m;
+  }
+  if (r < r1) {
+    if (key < 0) {
+      inv_perm[r] = -1;
+    } else if (key < S) {
+      perm[pos] = r;
+      inv_perm[r] = pos;
+    } else {
+      inv_perm[r] = -1;
+      miss_token[pos] = r / k;
+      miss_expert[pos] = e;
+      miss_weight[pos] = topk_w[r];
+    }
+  }
 }
 
 __device__ void permute_body(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
@@ -49,14 +103,7 @@ __device__ void permute_body(const int32_t* topk_idx, const float* topk_w, int T
   if (tid == 0) bad = 0;
   __syncthreads();
 
-  // key of a row: slot, S for a miss, -1 for an invalid row
-  auto key_of = [&](int r, int& e) -> int {
-    e = topk_idx[r];
-    if (e < 0 || e >= E) return -1;
-    const int s = slot_map ? slot_map[e] : e;
-    if (s < -1 || s >= S) return -1;
-    return s < 0 ? S : s;
-  };
+  auto key_of = [&](int r, int& e) -> int { return row_key(topk_idx, E, slot_map, S, r, e); };
 
   // 1. counts
   for (int r = r0 + lane; r < r1; r += 64) {
@@ -122,35 +169,9 @@ __device__ void permute_body(const int32_t* topk_idx, const float* topk_w, int T
   __syncthreads();
 
   // 3. stable scatter
-  for (int c0 = r0; c0 < r1; c0 += 64) {
-    const int r = c0 + lane;
-    int e = 0, key = -1;
-    if (r < r1) key = key_of(r, e);
-    unsigned long long todo = __ballot(key >= 0);
-    int pos = -1;
-    while (todo) {
-      const int leader = __ffsll((long long)todo) - 1;
-      const int lkey = __shfl(key, leader);
-      const unsigned long long m = __ballot(key == lkey);
-      const int b = cnt[wid * K1 + lkey];
-      if (key == lkey) pos = b + __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == leader) cnt[wid * K1 + lkey] = b + __popcll(m);
-      todo &= ~m;
-    }
-    if (r < r1) {
-      if (key < 0) {
-        inv_perm[r] = -1;
-      } else if (key < S) {
-        perm[pos] = r;
-        inv_perm[r] = pos;
-      } else {
-        inv_perm[r] = -1;
-        miss_token[pos] = r / k;
-        miss_expert[pos] = e;
-        miss_weight[pos] = topk_w[r];
-      }
-    }
-  }
+  for (int c0 = r0; c0 < r1; c0 += 64)
+    scatter_chunk(topk_idx, topk_w, k, E, slot_map, S, c0, r1, cnt + wid * K1, perm, inv_perm, miss_token,
+                  miss_expert, miss_weight);
 
   // outputs of the scan and histogram
   for (int i = tid; i < E; i += kPermThreads) counts[i] = ecnt[i];
@@ -204,22 +225,181 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
                miss_token, miss_expert, miss_weight, err, scratch);
 }
 
+static hipError_t set_lds(const void* kern, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+}
+
+// ---- multi-group permutation -----------------------------------------------------------------
+// table row of group g: [K1 key counts (bases after the scan)][E expert counts][invalid flag]
+__host__ __device__ inline int perm_table_stride(int E, int S) { return S + 1 + E + 1; }
+
+// (1) per-group counts
+__global__ __launch_bounds__(kPermThreads) void perm_count_kernel(const int32_t* __restrict__ topk_idx, int R,
+                                                                  int E, const int32_t* __restrict__ slot_map,
+                                                                  int S, int32_t* __restrict__ table) {
+  extern __shared__ int32_t lds[];
+  const int K1 = S + 1, stride = perm_table_stride(E, S);
+  int32_t* cnt = lds;        // [K1]
+  int32_t* ecnt = lds + K1;  // [E]
+  __shared__ uint32_t bad;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < K1 + E; i += kPermThreads) lds[i] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  const int r = blockIdx.x * kPermThreads + tid;
+  if (r < R) {
+    int e;
+    const int key = row_key(topk_idx, E, slot_map, S, r, e);
+    if (key < 0) {
+      bad = 1;
+    } else {
+      atomicAdd(&cnt[key], 1);
+      atomicAdd(&ecnt[e], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* row = table + size_t(blockIdx.x) * stride;
+  for (int i = tid; i < K1 + E; i += kPermThreads) row[i] = lds[i];
+  if (tid == 0) row[K1 + E] = bad ? 1 : 0;
+}
+
+// (2) totals, slot offsets, per-group bases (one work-group)
+__global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(int32_t* __restrict__ table, int ngroups, int E,
+                                                                 int S, int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ slot_offsets,
+                                                                 int32_t* __restrict__ miss_count,
+                                                                 uint32_t* __restrict__ err) {
+  extern __shared__ int32_t tot[];  // [K1 + 1]
+  __shared__ int32_t wsum[kPermWaves];
+  __shared__ uint32_t bad;
+  const int K1 = S + 1, stride = perm_table_stride(E, S);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int key = tid; key < K1 + E + 1; key += kPermThreads) {
+    int s = 0;
+#pragma unroll 8
+    for (int g = 0; g < ngroups; ++g) s += table[size_t(g) * stride + key];
+    if (key < K1) tot[key] = s;
+    else if (key < K1 + E) counts[key - K1] = s;
+    else if (s) bad = 1;
+  }
+  __syncthreads();
+  // exclusive scan of the S slot totals (the miss key scans separately from 0)
+  {
+    const int per = (S + kPermThreads - 1) / kPermThreads;
+    const int a = tid * per, b = min(S, a + per);
+    int local = 0;
+    for (int i = a; i < b; ++i) local += tot[i];
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wid; ++w) wbase += wsum[w];
+    int run = wbase + incl - local;
+    __syncthreads();
+    for (int i = a; i < b; ++i) {
+      const int c = tot[i];
+      tot[i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // group bases per key, groups in row order
+  for (int key = tid; key < K1; key += kPermThreads) {
+    int run = key == S ? 0 : tot[key];
+    for (int g = 0; g < ngroups; ++g) {
+      int32_t* c = table + size_t(g) * stride + key;
+      const int v = *c;
+      *c = run;
+      run += v;
+    }
+  }
+  for (int i = tid; i < S; i += kPermThreads) slot_offsets[i] = tot[i];
+  if (tid == 0) {
+    int n_res = 0;
+    for (int w = 0; w < kPermWaves; ++w) n_res += wsum[w];
+    slot_offsets[S] = n_res;
+    if (miss_count) miss_count[0] = tot[S];
+    err[0] = bad ? 1u : 0u;
+  }
+}
+
+// (3) per-group stable scatter from the group's bases
+__global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int R, int k, int E,
+    const int32_t* __restrict__ slot_map, int S, const int32_t* __restrict__ table, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ miss_token, int32_t* __restrict__ miss_expert,
+    float* __restrict__ miss_weight) {
+  extern __shared__ int32_t cnt[];  // [kPermWaves][K1]
+  const int K1 = S + 1, stride = perm_table_stride(E, S);
+  const int tid = threadIdx.x, wid = tid >> 6;
+  for (int i = tid; i < kPermWaves * K1; i += kPermThreads) cnt[i] = 0;
+  __syncthreads();
+  const int r0 = blockIdx.x * kPermThreads, r1 = min(R, r0 + kPermThreads);
+  const int r = r0 + tid;
+  if (r < r1) {
+    int e;
+    const int key = row_key(topk_idx, E, slot_map, S, r, e);
+    if (key >= 0) atomicAdd(&cnt[wid * K1 + key], 1);
+  }
+  __syncthreads();
+  const int32_t* base = table + size_t(blockIdx.x) * stride;
+  for (int key = tid; key < K1; key += kPermThreads) {
+    int run = base[key];
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = cnt[w * K1 + key];
+      cnt[w * K1 + key] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const int c0 = r0 + wid * 64;
+  if (c0 < r1)
+    scatter_chunk(topk_idx, topk_w, k, E, slot_map, S, c0, r1, cnt + wid * K1, perm, inv_perm, miss_token,
+                  miss_expert, miss_weight);
+}
+
+size_t permute_scratch_bytes(int T, int k, int E, int S) {
+  const long long R = (long long)T * k;
+  if (R <= kPermOneGroupRows) return 0;
+  const long long groups = (R + kPermThreads - 1) / kPermThreads;
+  return size_t(groups) * perm_table_stride(E, S) * sizeof(int32_t);
+}
+
 size_t permute_lds_bytes(int E, int S) { return sizeof(int32_t) * permute_lds_words(E, S); }
 
 size_t route_permute_lds_bytes(int T, int k, int E, int S) {
   return sizeof(int32_t) * (size_t(2) * T * k + permute_lds_words(E, S));
 }
 
-static hipError_t set_lds(const void* kern, size_t lds) {
-  if (lds <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-}
-
 hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
                           const int32_t* slot_map, int S, int32_t* counts, int32_t* slot_offsets,
                           int32_t* perm, int32_t* inv_perm, int32_t* miss_count,
                           int32_t* miss_token, int32_t* miss_expert, float* miss_weight,
-                          uint32_t* err, hipStream_t st) {
+                          uint32_t* err, int32_t* scratch, hipStream_t st) {
+  const int R = T * k;
+  if (R > kPermOneGroupRows) {
+    const int groups = (R + kPermThreads - 1) / kPermThreads;
+    const size_t l1 = sizeof(int32_t) * size_t(S + 1 + E);
+    const size_t l2 = sizeof(int32_t) * size_t(S + 2);
+    const size_t l3 = sizeof(int32_t) * size_t(kPermWaves) * (S + 1);
+    hipError_t e = set_lds((const void*)perm_count_kernel, l1);
+    if (e == hipSuccess) e = set_lds((const void*)perm_scan_kernel, l2);
+    if (e == hipSuccess) e = set_lds((const void*)perm_scatter_kernel, l3);
+    if (e != hipSuccess) return e;
+    perm_count_kernel<<<groups, kPermThreads, l1, st>>>(topk_idx, R, E, slot_map, S, scratch);
+    perm_scan_kernel<<<1, kPermThreads, l2, st>>>(scratch, groups, E, S, counts, slot_offsets, miss_count, err);
+    perm_scatter_kernel<<<groups, kPermThreads, l3, st>>>(topk_idx, topk_w, R, k, E, slot_map, S, scratch, perm,
+                                                          inv_perm, miss_token, miss_expert, miss_weight);
+    return hipGetLastError();
+  }
   const size_t lds = permute_lds_bytes(E, S);
   hipError_t e = set_lds((const void*)permute_kernel, lds);
   if (e != hipSuccess) return e;

@@ -8,14 +8,15 @@ namespace moe {
 
 // ---------------------------------------------------------------------------------------------
 // logits[t, e] = sum_h x[t,h] W_r[e,h] (+ bias[e])
-// One work-group per expert row: its 256 threads stride the row in 16-byte chunks (the row is
-// read from HBM once per batch of kRouterTok tokens), partial sums are reduced with DPP inside
-// each wave and across the four waves through LDS.
+// One work-group per expert row: thread j owns the row's 16-byte chunks j, j+256, ... (NCH of
+// them, H <= 1024*NCH), loaded once, all in flight together; the activations of kRouterTok tokens
+// are loaded likewise before any arithmetic.  Partial sums are reduced with DPP inside each wave
+// and across the four waves through LDS.
 // ---------------------------------------------------------------------------------------------
 constexpr int kRouterThreads = 256;
 constexpr int kRouterTok = 8;
 
-template <int XDT>
+template <int XDT, int NCH>
 __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const void* __restrict__ x_,
                                                                        const float* __restrict__ wr,
                                                                        const float* __restrict__ bias,
@@ -27,42 +28,50 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const voi
   const float4* wrow = reinterpret_cast<const float4*>(wr + size_t(e) * H);
   const int nch = H >> 2;
   const float b = bias ? bias[e] : 0.0f;
+  // chunks past the row re-read its last chunk and are weighted by zero
+  float4 w[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tid + kRouterThreads * j;
+    w[j] = wrow[min(c, nch - 1)];
+    if (c >= nch) w[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
   for (int t0 = 0; t0 < T; t0 += kRouterTok) {
-    const int nt = min(kRouterTok, T - t0);
     float acc[kRouterTok];
 #pragma unroll
-    for (int i = 0; i < kRouterTok; ++i) acc[i] = 0.0f;
-    for (int c = tid; c < nch; c += kRouterThreads) {
-      const float4 w = wrow[c];
+    for (int i = 0; i < kRouterTok; ++i) {
+      const int t = min(t0 + i, T - 1);  // tokens past T repeat the last one (not stored)
+      float4 xv[NCH];
 #pragma unroll
-      for (int i = 0; i < kRouterTok; ++i) {
-        if (i < nt) {
-          float4 xv;
-          if constexpr (XDT == DT_F32) {
-            xv = reinterpret_cast<const float4*>(static_cast<const float*>(x_) + size_t(t0 + i) * H)[c];
-          } else {
-            const uint2 u = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x_) + size_t(t0 + i) * H)[c];
-            xv = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
-          }
-          acc[i] = fmaf(w.x, xv.x, acc[i]);
-          acc[i] = fmaf(w.y, xv.y, acc[i]);
-          acc[i] = fmaf(w.z, xv.z, acc[i]);
-          acc[i] = fmaf(w.w, xv.w, acc[i]);
+      for (int j = 0; j < NCH; ++j) {
+        const int c = min(tid + kRouterThreads * j, nch - 1);
+        if constexpr (XDT == DT_F32) {
+          xv[j] = reinterpret_cast<const float4*>(static_cast<const float*>(x_) + size_t(t) * H)[c];
+        } else {
+          const uint2 u = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x_) + size_t(t) * H)[c];
+          xv[j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
         }
       }
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        a = fmaf(w[j].x, xv[j].x, a);
+        a = fmaf(w[j].y, xv[j].y, a);
+        a = fmaf(w[j].z, xv[j].z, a);
+        a = fmaf(w[j].w, xv[j].w, a);
+      }
+      acc[i] = a;
     }
 #pragma unroll
     for (int i = 0; i < kRouterTok; ++i) {
-      if (i < nt) {
-        const float s = seg_sum<64>(acc[i]);
-        if (lane == 63) part[wid][i] = s;
-      }
+      const float s = seg_sum<64>(acc[i]);
+      if (lane == 63) part[wid][i] = s;
     }
     __syncthreads();
-    if (tid < nt) {
+    if (tid < kRouterTok && t0 + tid < T) {
       float s = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kRouterThreads / 64; ++w) s += part[w][tid];
+      for (int w2 = 0; w2 < kRouterThreads / 64; ++w2) s += part[w2][tid];
       logits[size_t(t0 + tid) * E + e] = s + b;
     }
     __syncthreads();
@@ -93,10 +102,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 hipError_t launch_router_logits(const void* x, int xdt, const float* wr, const float* bias,
                                 float* logits, int T, int H, int E, hipStream_t st) {
   dim3 grid(E), block(kRouterThreads);
-  if (xdt == DT_F32)
-    router_logits_kernel<DT_F32><<<grid, block, 0, st>>>(x, wr, bias, logits, T, H, E);
-  else
-    router_logits_kernel<DT_BF16><<<grid, block, 0, st>>>(x, wr, bias, logits, T, H, E);
+  const int nch = (H / 4 + kRouterThreads - 1) / kRouterThreads;  // chunks per thread
+#define MOE_ROUTER_LAUNCH(N)                                                                    \
+  {                                                                                             \
+    if (xdt == DT_F32)                                                                          \
+      router_logits_kernel<DT_F32, N><<<grid, block, 0, st>>>(x, wr, bias, logits, T, H, E);    \
+    else                                                                                        \
+      router_logits_kernel<DT_BF16, N><<<grid, block, 0, st>>>(x, wr, bias, logits, T, H, E);   \
+  }
+  if (nch <= 1) MOE_ROUTER_LAUNCH(1)
+  else if (nch <= 2) MOE_ROUTER_LAUNCH(2)
+  else if (nch <= 4) MOE_ROUTER_LAUNCH(4)
+  else MOE_ROUTER_LAUNCH(8)
+#undef MOE_ROUTER_LAUNCH
   return hipGetLastError();
 }
 

@@ -13,17 +13,19 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
                                           int E, int k, int score, int renorm, int& my_e, float& my_w) {
   const int lane = threadIdx.x & 63;
   const float NEG = -__builtin_huge_valf();
+  // every load is issued before the first use (indices clamped, lanes past E masked afterwards)
   float v[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = lane + 64 * i;
-    float l = NEG;
-    if (e < E) {
-      l = lrow[e];
-      if (bias) l += bias[e];
-    }
-    v[i] = l;
+  for (int i = 0; i < VPL; ++i) v[i] = lrow[min(lane + 64 * i, E - 1)];
+  if (bias) {
+    float b[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) b[i] = bias[min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] += b[i];
   }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) v[i] = lane + 64 * i < E ? v[i] : NEG;
   float mx = 0.0f, z = 1.0f;
   if (score == 0) {  // softmax statistics over all E
     float m = NEG;
@@ -45,11 +47,10 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int e = lane + 64 * i;
-      const bool better = v[i] > bv || (v[i] == bv && e < bi);
-      if (e < E && !((taken >> i) & 1u) && better) {
-        bv = v[i];
-        bi = e;
-      }
+      const bool better = (v[i] > bv) | ((v[i] == bv) & (e < bi));
+      const bool ok = (e < E) & !((taken >> i) & 1u) & better;
+      bv = ok ? v[i] : bv;
+      bi = ok ? e : bi;
     }
     wave_argmax(bv, bi);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);

@@ -19,15 +19,36 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
   const int h = (blockIdx.y * kCombThreads + threadIdx.x) * 4;
   if (h >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int p = inv[size_t(t) * k + j];
-    if (p < 0 || p >= cap) continue;
-    const float g = w[size_t(t) * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + size_t(p) * H + h);
-    acc.x = fmaf(g, v.x, acc.x);
-    acc.y = fmaf(g, v.y, acc.y);
-    acc.z = fmaf(g, v.z, acc.z);
-    acc.w = fmaf(g, v.w, acc.w);
+  // the token's positions and gates, one per lane (k <= 64), in one load each; then groups of kJ
+  // choices: every row load of a group in flight together, the sums in ascending j
+  const int lane = threadIdx.x & 63;
+  const int pv = lane < k ? inv[size_t(t) * k + lane] : -1;
+  const float gv = lane < k ? w[size_t(t) * k + lane] : 0.0f;
+  constexpr int kJ = 8;
+  for (int j0 = 0; j0 < k; j0 += kJ) {
+    int p[kJ];
+    float g[kJ];
+#pragma unroll
+    for (int u = 0; u < kJ; ++u) {
+      p[u] = __builtin_amdgcn_readlane(pv, j0 + u);
+      g[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j0 + u));
+      if (j0 + u >= k || p[u] >= cap) p[u] = -1;
+    }
+    float4 v[kJ];
+#pragma unroll
+    for (int u = 0; u < kJ; ++u) {
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p[u] >= 0) v[u] = *reinterpret_cast<const float4*>(y + size_t(p[u]) * H + h);
+    }
+#pragma unroll
+    for (int u = 0; u < kJ; ++u) {
+      if (p[u] >= 0) {
+        acc.x = fmaf(g[u], v[u].x, acc.x);
+        acc.y = fmaf(g[u], v[u].y, acc.y);
+        acc.z = fmaf(g[u], v[u].z, acc.z);
+        acc.w = fmaf(g[u], v[u].w, acc.w);
+      }
+    }
   }
   if constexpr (ODT == DT_F32) {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + size_t(t) * H + h) = acc;

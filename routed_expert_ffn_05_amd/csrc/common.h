@@ -119,28 +119,27 @@ __device__ __forceinline__ float wave_max_all(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Wave-wide best (value descending, index ascending); every lane receives the winner.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  const int NEG = __float_as_int(-__builtin_huge_valf());
-  const int BIG = 0x7FFFFFFF;
-#define MOE_ARGMAX_STEP(CTRL, RM)                                                 \
-  {                                                                               \
-    const float ov = __int_as_float(dpp_src_or<CTRL, RM>(NEG, __float_as_int(v))); \
-    const int oi = dpp_src_or<CTRL, RM>(BIG, i);                                  \
-    const bool take = (ov > v) | ((ov == v) & (oi < i));                          \
-    v = take ? ov : v;                                                            \
-    i = take ? oi : i;                                                            \
+// Unsigned 64-bit maximum over the wave, returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#define MOE_MAXU64_STEP(CTRL, RM)                                                        \
+  {                                                                                      \
+    const uint32_t oh = uint32_t(dpp_src_or<CTRL, RM>(0, int(uint32_t(v >> 32))));      \
+    const uint32_t ol = uint32_t(dpp_src_or<CTRL, RM>(0, int(uint32_t(v))));             \
+    const uint64_t o = (uint64_t(oh) << 32) | ol;                                        \
+    v = o > v ? o : v;                                                                   \
   }
-  MOE_ARGMAX_STEP(0x111, 0xF)
-  MOE_ARGMAX_STEP(0x112, 0xF)
-  MOE_ARGMAX_STEP(0x114, 0xF)
-  MOE_ARGMAX_STEP(0x118, 0xF)
-  MOE_ARGMAX_STEP(0x142, 0xA)
-  MOE_ARGMAX_STEP(0x143, 0xC)
-#undef MOE_ARGMAX_STEP
-  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  i = __builtin_amdgcn_readlane(i, 63);
+  MOE_MAXU64_STEP(0x111, 0xF)
+  MOE_MAXU64_STEP(0x112, 0xF)
+  MOE_MAXU64_STEP(0x114, 0xF)
+  MOE_MAXU64_STEP(0x118, 0xF)
+  MOE_MAXU64_STEP(0x142, 0xA)
+  MOE_MAXU64_STEP(0x143, 0xC)
+#undef MOE_MAXU64_STEP
+  const uint32_t h = __builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63);
+  const uint32_t l = __builtin_amdgcn_readlane(int(uint32_t(v)), 63);
+  return (uint64_t(h) << 32) | l;
 }
+
 
 // ---------------------------------------------------------------------------------------------
 // active-slot lookup: the ord-th slot with a non-empty row range in off[0..S]

@@ -35,7 +35,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxDim = 8192;
 constexpr long long kMaxRows = 1LL << 26;  // T*k
-constexpr int kFusedRouteMaxT = 64;       // batches up to this size route and permute in one launch
+constexpr int kFusedRouteMaxT = 16;       // batches up to this size (a token per wave) route and permute in one launch
 
 int elems_per_chunk(int wdtype) {
   switch (wdtype) {

@@ -38,29 +38,41 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
       if (lane + 64 * i < E) zs += expf(v[i] - mx);
     z = wave_total(zs);
   }
-  unsigned taken = 0;  // bit i: v[i] already selected
-  float my_s = 0.0f, ssum = 0.0f;
+  // Selection key per value: orderable logit bits (high word; -0 taken as +0), inverted expert id
+  // (low word), so the unsigned maximum is the largest logit with the smallest id.  A selected or
+  // absent value gets key 0, below every real key.
+  uint64_t key[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    const uint32_t b = __float_as_uint(v[i] + 0.0f);
+    const uint32_t h = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    key[i] = e < E ? ((uint64_t(h) << 32) | uint32_t(~e)) : 0ull;
+  }
+  float my_l = 0.0f;
   my_e = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = NEG;
-    int bi = 0x7FFFFFFF;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = lane + 64 * i;
-      const bool better = (v[i] > bv) | ((v[i] == bv) & (e < bi));
-      const bool ok = (e < E) & !((taken >> i) & 1u) & better;
-      bv = ok ? v[i] : bv;
-      bi = ok ? e : bi;
+    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = int(~uint32_t(best));
+    const uint32_t h = uint32_t(best >> 32);
+    const float l = __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h);
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (i == (e >> 6)) key[i] = 0ull;
     }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    const float s = (score == 0) ? expf(bv - mx) / z : 1.0f / (1.0f + expf(-bv));
-    ssum += s;  // ascending j, the same on every lane
     if (lane == j) {
-      my_s = s;
-      my_e = bi;
+      my_l = l;
+      my_e = e;
     }
   }
+  // scores of the k chosen (lane j holds the j-th), gates renormalised in ascending j
+  const float my_s = (score == 0) ? expf(my_l - mx) / z : 1.0f / (1.0f + expf(-my_l));
+  float ssum = 0.0f;
+  for (int j = 0; j < k; ++j) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
   my_w = renorm ? my_s / ssum : my_s;
 }
 

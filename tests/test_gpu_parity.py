@@ -76,7 +76,7 @@ def test_permute_stage(small_case):
 
 
 def test_route_permute_stage(small_case):
-    # one launch for T <= 64 (top-k and permutation share a work-group), two above
+    # one launch for T <= 16 (top-k and permutation share a work-group), two or more above
     from gpu_cases import check_permute, check_routing
     name, inp, g, ref = small_case
     _banner(name + "/route_permute", inp.cfg)

@@ -66,9 +66,13 @@ typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scor
 typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 } moe_path;
 
 /* Expert-FFN arithmetic.  MODE_A: activations kept in bf16/fp32, weights decoded exactly,
- * fp32 accumulation.  MODE_B (GEMM path only): activations quantised per row and per 32
- * K-elements to E4M3 with an E8M0 scale 2^(floor(log2 amax) - 8), saturating at +-448, before
- * each projection, then low-precision MFMA. */
+ * fp32 accumulation.  MODE_B: the activations entering each projection (x before gate/up, a
+ * before down) are quantised per row and per 32 K-elements as moe_quantize_mx_e4m3 does.  The
+ * GEMM path then multiplies the E4M3 codes with the FP8 or MXFP4 weights on the block-scaled
+ * matrix cores (FP8 or MXFP4 weights only, H and I multiples of 64 and at most 4096); the GEMV
+ * path (any weight dtype, H and I multiples of 32) multiplies the dequantised values, which are
+ * exact in bf16/fp32.  Mode B is judged against the same quantisation applied in the reference
+ * model of the layer. */
 typedef enum moe_mode { MOE_MODE_A = 0, MOE_MODE_B = 1 } moe_mode;
 
 /* The expert weights of one layer, in device memory.  S = number of slots, H = hidden size,
@@ -203,6 +207,21 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
               int32_t* topk_idx, float* topk_w, int32_t* miss_count, int32_t* miss_token,
               int32_t* miss_expert, float* miss_weight, void* ws, size_t ws_bytes,
               void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_quantize_mx_e4m3 -- the mode-B activation quantisation, on its own (OCP MX rule with an
+ * E4M3 element type).  For each row and each 32 consecutive elements: X = floor(log2 amax) - 8
+ * (X = 0 for an all-zero block; X is kept >= -127), scale byte X + 127 (E8M0), codes = E4M3
+ * (e4m3fn) of v / 2^X rounded to nearest even and saturated at +-448.  Quantised value =
+ * code * 2^X exactly.
+ *   in      device [rows, K], in_dtype MOE_F32 or MOE_BF16, 16-byte aligned; K % 32 == 0
+ *   codes   device uint8 [rows, K] out, or NULL
+ *   scales  device uint8 [rows, K/32] out, or NULL
+ *   deq     device [rows, K] out of deq_dtype (MOE_F32 or MOE_BF16): the quantised values, or
+ *           NULL; may be `in` itself when in_dtype == deq_dtype == MOE_F32
+ * ------------------------------------------------------------------------------------------ */
+int moe_quantize_mx_e4m3(const void* in, int in_dtype, int rows, int K, uint8_t* codes, uint8_t* scales,
+                         void* deq, int deq_dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * helpers

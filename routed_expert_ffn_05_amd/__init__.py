@@ -62,6 +62,7 @@ _SIGS = {
     "moe_layer_workspace_size": (_Z, [_I, _R, _W, _I, _I, _I]),
     "moe_layer": (_I, [_P, _I, _I, _P, _P, _P, _R, _P, _W, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                        _P, _Z, _P]),
+    "moe_quantize_mx_e4m3": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P]),
     "moe_check_device_error": (_I, [_P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -195,6 +196,11 @@ def moe_expert_gate_up(w, x, x_dtype, T, k, perm, slot_offsets, path, mode, ws, 
 def moe_expert_down(w, T, k, slot_offsets, path, mode, y_perm, ws, ws_bytes, stream=None):
     _check(lib().moe_expert_down(_ref(w), T, k, _ptr(slot_offsets), path, mode, _ptr(y_perm), _ptr(ws),
                                  ws_bytes, _stream(stream)), "moe_expert_down")
+
+
+def moe_quantize_mx_e4m3(x, x_dtype, rows, K, codes=None, scales=None, deq=None, deq_dtype=MOE_F32, stream=None):
+    _check(lib().moe_quantize_mx_e4m3(_ptr(x), x_dtype, rows, K, _ptr(codes), _ptr(scales), _ptr(deq), deq_dtype,
+                                      _stream(stream)), "moe_quantize_mx_e4m3")
 
 
 def moe_combine(y_perm, inv_perm, topk_w, T, k, H, out, out_dtype, stream=None):

@@ -423,6 +423,299 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Mode B: block-scaled low-precision matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4).  A = E4M3
+// activation codes with one E8M0 scale per row and 32 K (quantised beforehand), B = the stored
+// weights: E4M3 (scale operand 1.0, the 128x128 block scale folded in per K block as in mode A)
+// or E2M1 with its own E8M0 scales.  One MFMA covers a 64-wide K step; operand lanes: lane (r, h)
+// holds 8-bit K granules h and 2+h (16 elements each) of the step, or 4-bit K [32h, 32h+32);
+// lane r+32b supplies the scale of K block b of row (column) r.
+// GATEUP = true:  A = quantised x rows (through perm), out a (fp32, quantised again before down)
+// GATEUP = false: A = quantised a rows (positions),    out y (fp32)
+// ---------------------------------------------------------------------------------------------
+template <int WD> struct QFmt {
+  static constexpr int ROW = WD == DT_FP8 ? 64 : 32;        // B bytes per row and K step
+  static constexpr int STAGE = BN * ROW;
+  static constexpr int INSTR = STAGE / (1024 * kWaves);
+  static constexpr int BUDGET = WD == DT_MXFP4 ? 104 * 1024 : 128 * 1024;
+  static constexpr int stage_bytes(int ns) { return ns * 2048 + STAGE; }  // A: 32*NS rows x 64 B
+  static constexpr int nstage(int ns) { return BUDGET / stage_bytes(ns) < 8 ? BUDGET / stage_bytes(ns) : 8; }
+};
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int WD, bool GATEUP>
+__global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
+    const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint8_t* __restrict__ aq,
+    const uint8_t* __restrict__ as, const int32_t* __restrict__ perm, const int32_t* __restrict__ off,
+    const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, int T, int k, int K, int N, int I,
+    float* __restrict__ out) {
+  static_assert(WD == DT_FP8 || WD == DT_MXFP4, "mode B weights");
+  using F = QFmt<WD>;
+  __shared__ __align__(16) uint8_t smem[F::BUDGET];
+  __shared__ float Ssc[4][64];                                                    // FP8 block scales
+  __shared__ __align__(16) uint8_t Sfp4[WD == DT_MXFP4 ? BN * kMaxFp4Kb : 16];    // weight E8M0
+  __shared__ __align__(16) uint8_t Sact[BM * kMaxFp4Kb];                          // activation E8M0
+  __shared__ uint8_t rowok[BM];
+  const int n_act = ntiles[0];
+  if (int(blockIdx.x) >= n_act) return;
+  const int2 ent = tiles[xcd_remap(blockIdx.x, n_act)];
+  const int s = ent.x, nt = ent.y & 0xFF, mt = ent.y >> 8;
+  const int cap = T * k;
+  const int lo = min(max(off[s], 0), cap), hi = min(max(off[s + 1], lo), cap);
+  const int m0 = lo + mt * BM;
+  const int rows = min(BM, hi - m0);
+  if (rows <= 0) return;
+  const int nsub = (rows + 31) >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, kh = lane >> 5;
+  const int n0 = GATEUP ? nt * (BN / 2) : nt * BN;
+  const size_t rb = row_bytes<WD>(K);
+  const uint8_t* wslot = w + size_t(s) * N * rb;
+  auto brow_global = [&](int r) -> int {
+    if constexpr (GATEUP) return r < BN / 2 ? n0 + r : I + n0 + (r - BN / 2);
+    return n0 + r;
+  };
+  auto brow_clamped = [&](int r) -> int { return min(brow_global(r), N - 1); };
+  // activation row of tile row r (a valid row for rows past the tile, never stored)
+  auto a_row = [&](int r) -> int {
+    int src = GATEUP ? 0 : m0;
+    if (r < rows) {
+      if constexpr (GATEUP) {
+        const int rr = perm[m0 + r];
+        src = (rr >= 0 && rr / k < T) ? rr / k : 0;
+      } else {
+        src = m0 + r;
+      }
+    }
+    return src;
+  };
+  // B sources: 64-byte rows: lane -> row 16c + lane/4 (fp8); 32-byte rows: row 32c + lane/2 (fp4)
+  const uint8_t* bsrc[F::INSTR];
+#pragma unroll
+  for (int j = 0; j < F::INSTR; ++j) {
+    const int c = F::INSTR * wv + j;
+    int r, g;
+    if constexpr (WD == DT_FP8) {
+      r = 16 * c + (lane >> 2);
+      g = swz64(r, lane & 3);
+    } else {
+      r = 32 * c + (lane >> 1);
+      g = swz32(r, lane & 1);
+    }
+    bsrc[j] = wslot + size_t(brow_clamped(r)) * rb + g * 16;
+  }
+  if (tid < BM) {
+    bool ok = tid < rows;
+    if constexpr (GATEUP) {
+      if (ok) {
+        const int rr = perm[m0 + tid];
+        ok = rr >= 0 && rr / k < T;
+      }
+    }
+    rowok[tid] = ok;
+  }
+  const int bl = GATEUP ? (ln < 16 ? 16 * wv + ln : BN / 2 + 16 * wv + (ln - 16)) : 32 * wv + ln;
+  int srow = 0;
+  if constexpr (WD == DT_FP8) {
+    const int KB = (K + 127) >> 7;
+    const int NBk = (N + 127) >> 7;
+    int blk[4];
+    blk[0] = brow_clamped(0) >> 7;
+    blk[1] = brow_clamped(127) >> 7;
+    blk[2] = brow_clamped(128) >> 7;
+    blk[3] = brow_clamped(255) >> 7;
+    const float* sbase = static_cast<const float*>(wscale) + size_t(s) * NBk * KB;
+    for (int t = tid; t < 4 * KB; t += kThreads) {
+      const int r = t / KB, kb = t - r * KB;
+      Ssc[r][kb] = sbase[size_t(blk[r]) * KB + kb];
+    }
+    const int gb = brow_clamped(bl) >> 7;
+    srow = gb == blk[0] ? 0 : gb == blk[1] ? 1 : gb == blk[2] ? 2 : 3;
+  }
+  // E8M0 rows (weights of the tile's columns; activations of its rows): [row][K/32] in LDS.  With
+  // K % 512 == 0 a row is gpr whole 16-byte granules, rotated by a per-row key so that the rows
+  // read together by one instruction fall in different LDS banks, and loaded by direct loads
+  // issued with the first stages; otherwise copied unrotated before the main loop.
+  const int KB32 = K >> 5;
+  const bool sc_async = KB32 % 16 == 0;
+  const int gpr = sc_async ? KB32 >> 4 : 1;
+  const int sc_d = sc_async ? 16 / (gpr & -gpr < 16 ? gpr & -gpr : 16) : 1;
+  auto sc_key = [&](int r) -> int { return sc_async ? (r / sc_d) % gpr : 0; };
+  auto sc_index = [&](int r, int kb) -> int {
+    if (!sc_async) return r * KB32 + kb;
+    int slot = (kb >> 4) + sc_key(r);
+    slot -= slot >= gpr ? gpr : 0;
+    return r * KB32 + slot * 16 + (kb & 15);
+  };
+  const uint8_t* fp4_src = WD == DT_MXFP4 ? static_cast<const uint8_t*>(wscale) + size_t(s) * N * KB32 : nullptr;
+  if (!sc_async) {
+    for (int t = tid; t < BM * KB32; t += kThreads) {
+      const int r = t / KB32, q = t - r * KB32;
+      Sact[t] = as[size_t(a_row(r)) * KB32 + q];
+    }
+    if constexpr (WD == DT_MXFP4) {
+      for (int t = tid; t < BN * KB32; t += kThreads) {
+        const int r = t / KB32, q = t - r * KB32;
+        Sfp4[t] = fp4_src[size_t(brow_clamped(r)) * KB32 + q];
+      }
+    }
+  }
+
+  const int nk = K / BK;
+
+  auto run = [&](auto ns_c) {
+    constexpr int NS = decltype(ns_c)::value;
+    constexpr int NA = 2 * NS;                        // A chunks (16 rows x 64 B) per step
+    constexpr int A_HI = (NA + kWaves - 1) / kWaves;
+    constexpr int A_LO = NA / kWaves;
+    constexpr int NST = F::nstage(NS);
+    constexpr int SB = F::stage_bytes(NS);
+    constexpr int AB = NS * 2048;
+    static_assert(NST >= 3, "LDS budget");
+    const int na = (NA % kWaves == 0 || wv < NA % kWaves) ? A_HI : A_LO;
+    const int nl = na + F::INSTR;
+    const uint8_t* asrc[A_HI > 0 ? A_HI : 1];
+#pragma unroll
+    for (int j = 0; j < (A_HI > 0 ? A_HI : 1); ++j) {
+      const int c = j < na ? wv + kWaves * j : 0;
+      const int r = 16 * c + (lane >> 2);
+      asrc[j] = aq + size_t(a_row(r)) * K + swz64(r, lane & 3) * 16;
+    }
+    const uint32_t lds0 = lds_addr(smem);
+    auto issue_one = [&](int j, int kk, uint32_t st) {
+      if (j < na) {
+#pragma unroll
+        for (int q = 0; q < A_HI; ++q)
+          if (q == j) dma16(asrc[q] + size_t(kk) * BK, st + (wv + kWaves * q) * 1024);
+      } else {
+#pragma unroll
+        for (int q = 0; q < F::INSTR; ++q)
+          if (q == j - na) dma16(bsrc[q] + size_t(kk) * (F::ROW), st + AB + (F::INSTR * wv + q) * 1024);
+      }
+    };
+    auto issue_step = [&](int kk, uint32_t st) {
+#pragma unroll
+      for (int j = 0; j < A_HI + F::INSTR; ++j)
+        if (j < nl) issue_one(j, kk, st);
+    };
+
+    f32x16_t acc[NS], tmp[NS];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ms][r] = tmp[ms][r] = 0.0f;
+
+    // prologue: side data visible, the scale rows and the first NST-1 steps in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (sc_async) {
+      const uint32_t la = lds_addr(Sact);
+      for (int c = wv; c * 64 < BM * gpr; c += kWaves) {
+        const int L = c * 64 + lane;
+        const int r = L / gpr, slot = L - r * gpr;
+        int q = slot - sc_key(r);
+        q += q < 0 ? gpr : 0;
+        dma16(as + size_t(a_row(r)) * KB32 + q * 16, la + c * 1024);
+      }
+      if constexpr (WD == DT_MXFP4) {
+        const uint32_t lb = lds_addr(Sfp4);
+        for (int c = wv; c * 64 < BN * gpr; c += kWaves) {
+          const int L = c * 64 + lane;
+          const int r = L / gpr, slot = L - r * gpr;
+          int q = slot - sc_key(r);
+          q += q < 0 ? gpr : 0;
+          dma16(fp4_src + size_t(brow_clamped(r)) * KB32 + q * 16, lb + c * 1024);
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p) issue_step(min(p, nk - 1), lds0 + p * SB);
+    int sr = 0, sw = NST - 1;
+    for (int kk = 0; kk < nk; ++kk) {
+      if (na == A_HI) wait_vmcnt<(A_HI + F::INSTR) * (NST - 2)>();
+      else wait_vmcnt<(A_LO + F::INSTR) * (NST - 2)>();
+      __builtin_amdgcn_s_barrier();
+      const uint8_t* st = smem + sr * SB;
+      const uint32_t wst = lds0 + sw * SB;
+      const int kn = min(kk + NST - 1, nk - 1);
+      sr = sr + 1 == NST ? 0 : sr + 1;
+      sw = sw + 1 == NST ? 0 : sw + 1;
+      // operands of this step: B (column bl), then per row block A and its scale
+      i32x8_t b;
+      const uint8_t* B = st + AB;
+      int sb = 127;
+      if constexpr (WD == DT_FP8) {
+        const uint4 q0 = *reinterpret_cast<const uint4*>(B + bl * 64 + swz64(bl, kh) * 16);
+        const uint4 q1 = *reinterpret_cast<const uint4*>(B + bl * 64 + swz64(bl, 2 + kh) * 16);
+        b[0] = q0.x; b[1] = q0.y; b[2] = q0.z; b[3] = q0.w;
+        b[4] = q1.x; b[5] = q1.y; b[6] = q1.z; b[7] = q1.w;
+      } else {
+        const uint4 q0 = *reinterpret_cast<const uint4*>(B + bl * 32 + swz32(bl, kh) * 16);
+        b[0] = q0.x; b[1] = q0.y; b[2] = q0.z; b[3] = q0.w;
+        b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+        sb = Sfp4[sc_index(bl, kk * 2 + kh)];
+      }
+      i32x8_t a[NS];
+      int sa[NS];
+#pragma unroll
+      for (int ms = 0; ms < NS; ++ms) {
+        const int m = ms * 32 + ln;
+        const uint4 q0 = *reinterpret_cast<const uint4*>(st + m * 64 + swz64(m, kh) * 16);
+        const uint4 q1 = *reinterpret_cast<const uint4*>(st + m * 64 + swz64(m, 2 + kh) * 16);
+        a[ms][0] = q0.x; a[ms][1] = q0.y; a[ms][2] = q0.z; a[ms][3] = q0.w;
+        a[ms][4] = q1.x; a[ms][5] = q1.y; a[ms][6] = q1.z; a[ms][7] = q1.w;
+        sa[ms] = Sact[sc_index(m, kk * 2 + kh)];
+      }
+      issue_step(kn, wst);
+#pragma unroll
+      for (int ms = 0; ms < NS; ++ms) {
+        if constexpr (WD == DT_FP8)
+          tmp[ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ms], b, tmp[ms], 0, 0, 0, sa[ms], 0, sb);
+        else
+          acc[ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ms], b, acc[ms], 0, 4, 0, sa[ms], 0, sb);
+      }
+      if constexpr (WD == DT_FP8) {
+        if (((kk + 1) * BK) % 128 == 0 || kk + 1 == nk) {
+          const float sc = Ssc[srow][(kk * BK) >> 7];
+#pragma unroll
+          for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              acc[ms][r] = fmaf(sc, tmp[ms][r], acc[ms][r]);
+              tmp[ms][r] = 0.0f;
+            }
+        }
+      }
+    }
+    wait_vmcnt<0>();
+
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const float v = acc[ms][r];
+        if constexpr (GATEUP) {
+          const float o = __shfl_xor(v, 16);
+          if (ln < 16 && m < rows) {
+            const int i = n0 + 16 * wv + ln;
+            if (i < I) out[size_t(m0 + m) * I + i] = rowok[m] ? silu(v) * o : 0.0f;
+          }
+        } else {
+          const int h = n0 + 32 * wv + ln;
+          if (m < rows && h < N) out[size_t(m0 + m) * N + h] = v;
+        }
+      }
+    }
+  };
+  switch (nsub) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    default: run(std::integral_constant<int, 4>{}); break;
+  }
+}
+
 // fp32 activations -> bf16 (nearest even) for the matrix-core path
 __global__ void cast_bf16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, size_t n) {
   for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
@@ -546,6 +839,42 @@ static hipError_t down_t(const GemmArgs& g, hipStream_t st) {
       static_cast<const uint8_t*>(g.w_d), g.s_d, static_cast<const uint16_t*>(g.a), nullptr, g.off, g.tiles_dn,
       g.counts + 1, g.T, g.k, g.I, g.H, g.I, g.y);
   return hipGetLastError();
+}
+
+template <int WD>
+static hipError_t gate_up_q_t(const GemmArgs& g, hipStream_t st) {
+  const size_t grid = gemm_tiles_max(g.T, g.k, g.S, gemm_nt_gate_up(g.I));
+  if (grid == 0) return hipSuccess;
+  gemm::gemm_q_kernel<WD, true><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
+      static_cast<const uint8_t*>(g.w_gu), g.s_gu, g.xq, g.xs, g.perm, g.off, g.tiles_gu, g.counts, g.T, g.k,
+      g.H, 2 * g.I, g.I, static_cast<float*>(g.a));
+  return hipGetLastError();
+}
+
+template <int WD>
+static hipError_t down_q_t(const GemmArgs& g, hipStream_t st) {
+  const size_t grid = gemm_tiles_max(g.T, g.k, g.S, gemm_nt_down(g.H));
+  if (grid == 0) return hipSuccess;
+  gemm::gemm_q_kernel<WD, false><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
+      static_cast<const uint8_t*>(g.w_d), g.s_d, g.aq, g.as, nullptr, g.off, g.tiles_dn, g.counts + 1, g.T, g.k,
+      g.I, g.H, g.I, g.y);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_gate_up_q(const GemmArgs& g, hipStream_t st) {
+  switch (g.wdt) {
+    case DT_FP8: return gate_up_q_t<DT_FP8>(g, st);
+    case DT_MXFP4: return gate_up_q_t<DT_MXFP4>(g, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_down_q(const GemmArgs& g, hipStream_t st) {
+  switch (g.wdt) {
+    case DT_FP8: return down_q_t<DT_FP8>(g, st);
+    case DT_MXFP4: return down_q_t<DT_MXFP4>(g, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t st) {

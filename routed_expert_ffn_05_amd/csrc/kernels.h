@@ -55,8 +55,13 @@ struct GemmArgs {
   void* xb;             // [T, H] bf16 scratch: fp32 activations rounded once for the matrix cores
   const int32_t* perm;
   const int32_t* off;
-  void* a;              // [T*k, I] bf16
+  void* a;              // [T*k, I] bf16 (mode A) or fp32 (mode B)
   float* y;             // [T*k, H] fp32
+  // mode B: E4M3 codes and E8M0 scales (per row and 32 K) of x and a
+  uint8_t* xq;          // [T, H]
+  uint8_t* xs;          // [T, H/32]
+  uint8_t* aq;          // [T*k, I]
+  uint8_t* as;          // [T*k, I/32]
   int2* tiles_gu;       // tile lists written by the scheduler
   int2* tiles_dn;
   int32_t* counts;      // [2]: tiles of each GEMM
@@ -67,6 +72,17 @@ int gemm_nt_down(int H);
 hipError_t launch_gemm_schedule(const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm_gate_up(const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm_down(const GemmArgs& g, hipStream_t st);
+// mode B (FP8 / MXFP4 weights, quantised activations xq/xs and aq/as)
+hipError_t launch_gemm_gate_up_q(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_down_q(const GemmArgs& g, hipStream_t st);
+
+// Mode B activation quantisation of `rows` rows of K elements (K % 32 == 0): per 32 consecutive
+// elements an E8M0 scale 2^X, X = floor(log2 amax) - 8 (0 for an all-zero block), and E4M3 codes
+// of v / 2^X (nearest even, saturating at +-448).  Writes codes [rows][K] and scales
+// [rows][K/32] when non-null, and the dequantised values (code * 2^X, exact) to deq (bf16 or
+// fp32, may alias an fp32 input) when non-null.  Rows at or beyond *nrows (when given) are skipped.
+hipError_t launch_act_quant(const void* in, int in_dt, int rows, int K, const int32_t* nrows, uint8_t* codes,
+                            uint8_t* scales, void* deq, int deq_dt, hipStream_t st);
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int T, int k, int H,
                           void* out, int odt, hipStream_t st);

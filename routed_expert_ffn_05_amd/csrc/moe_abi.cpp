@@ -93,19 +93,22 @@ int check_weights(const moe_weights* w) {
   return MOE_OK;
 }
 
-// the matrix-core path needs bf16-exact weights, K steps of 64 and (MXFP4) the per-row E8M0
-// scales of K <= 4096 staged in LDS
-bool gemm_capable(const moe_weights* w) {
+// The matrix-core path needs K steps of 64 and, where E8M0 scale rows are staged in LDS (MXFP4
+// weights, mode B activations), K <= 4096.  Mode A decodes weights to bf16 exactly (bf16, FP8 or
+// MXFP4 weights); mode B multiplies E4M3 activations with FP8 or MXFP4 weights.
+bool gemm_capable(const moe_weights* w, int mode) {
   if (w->wdtype == MOE_F32 || w->H % 64 || w->I % 64) return false;
-  if (w->wdtype == MOE_MXFP4 && (w->H > 4096 || w->I > 4096)) return false;
+  const bool small_k = w->H <= 4096 && w->I <= 4096;
+  if (mode == MOE_MODE_B) return (w->wdtype == MOE_FP8_E4M3_B128 || w->wdtype == MOE_MXFP4) && small_k;
+  if (w->wdtype == MOE_MXFP4 && !small_k) return false;
   return true;
 }
 
 // AUTO: the GEMM path once slots hold several rows on average (measured crossover: the GEMV
 // streams weights at the same rate but re-reads them per group of rows)
-int resolve_path(int path, int T, int k, const moe_weights* w) {
+int resolve_path(int path, int T, int k, const moe_weights* w, int mode) {
   if (path != MOE_PATH_AUTO) return path;
-  if (gemm_capable(w) && (long long)T * k > 4LL * w->S) return MOE_PATH_GEMM;
+  if (gemm_capable(w, mode) && (long long)T * k > 4LL * w->S) return MOE_PATH_GEMM;
   return MOE_PATH_GEMV;
 }
 
@@ -113,10 +116,13 @@ int check_path_mode(int path, int mode, const moe_weights* w) {
   if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_GEMM)
     return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
   if (mode != MOE_MODE_A && mode != MOE_MODE_B) return fail(MOE_ERR_INVALID_ARG, "unknown mode %d", mode);
-  if (path == MOE_PATH_GEMM && !gemm_capable(w))
-    return fail(MOE_ERR_UNSUPPORTED, "the GEMM path needs bf16, FP8 or MXFP4 weights, H and I multiples of 64 "
-                                     "(and at most 4096 for MXFP4)");
-  if (mode == MOE_MODE_B) return fail(MOE_ERR_UNSUPPORTED, "mode B is not available in this build");
+  if (mode == MOE_MODE_B && (w->H % 32 || w->I % 32))
+    return fail(MOE_ERR_UNSUPPORTED, "mode B needs H and I multiples of 32 (one E8M0 scale per 32 elements)");
+  if (path == MOE_PATH_GEMM && !gemm_capable(w, mode))
+    return fail(MOE_ERR_UNSUPPORTED, mode == MOE_MODE_B
+                                         ? "the mode-B GEMM path needs FP8 or MXFP4 weights, H and I multiples of 64, at most 4096"
+                                         : "the GEMM path needs bf16, FP8 or MXFP4 weights, H and I multiples of 64 "
+                                           "(and at most 4096 for MXFP4)");
   return MOE_OK;
 }
 
@@ -133,30 +139,39 @@ struct Carve {
   }
 };
 
-// expert-FFN workspace: [256: header][a: T*k*I fp32 (GEMV) or bf16 (GEMM)][tile lists][counts]
+// expert-FFN workspace: [256: header][a: T*k*I fp32][xb: T*H bf16][tile lists][counts]
+// and, in mode B, [xq: T*H][xs: T*H/32][aq: T*k*I][as: T*k*I/32] (E4M3 codes, E8M0 scales)
 struct FfnWs {
   void* a;
   void* xb;
   int2* tiles_gu;
   int2* tiles_dn;
   int32_t* counts;
+  uint8_t *xq, *xs, *aq, *as;
   size_t used;
 };
-FfnWs carve_ffn(void* ws, const moe_weights* w, int T, int k) {
+FfnWs carve_ffn(void* ws, const moe_weights* w, int T, int k, int mode) {
   Carve c(ws);
   FfnWs f{};
+  const size_t R = size_t(T) * k;
   c.take<char>(256);
-  f.a = c.take<char>(size_t(T) * k * w->I * sizeof(float));
+  f.a = c.take<char>(R * w->I * sizeof(float));
   f.xb = c.take<char>(size_t(T) * w->H * 2);
   f.tiles_gu = c.take<int2>(moe::gemm_tiles_max(T, k, w->S, moe::gemm_nt_gate_up(w->I)) * sizeof(int2));
   f.tiles_dn = c.take<int2>(moe::gemm_tiles_max(T, k, w->S, moe::gemm_nt_down(w->H)) * sizeof(int2));
   f.counts = c.take<int32_t>(2 * sizeof(int32_t));
+  if (mode == MOE_MODE_B) {
+    f.xq = c.take<uint8_t>(size_t(T) * w->H);
+    f.xs = c.take<uint8_t>(size_t(T) * w->H / 32);
+    f.aq = c.take<uint8_t>(R * w->I);
+    f.as = c.take<uint8_t>(R * w->I / 32);
+  }
   f.used = c.used;
   return f;
 }
-size_t ffn_ws_size(const moe_weights* w, int T, int k, int path) {
+size_t ffn_ws_size(const moe_weights* w, int T, int k, int path, int mode) {
   (void)path;
-  return carve_ffn(nullptr, w, T, k).used;
+  return carve_ffn(nullptr, w, T, k, mode).used;
 }
 
 #define MOE_TRY(expr)           \
@@ -261,9 +276,8 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, int T, const moe_r
 
 // ---------------------------------------------------------------------------------------------
 size_t moe_expert_ffn_workspace_size(const moe_weights* w, int T, int k, int path, int mode) {
-  (void)mode;
   if (!w || T < 0 || k < 1 || w->I < 1) return 0;
-  return ffn_ws_size(w, T, k, resolve_path(path, T, k, w));
+  return ffn_ws_size(w, T, k, resolve_path(path, T, k, w, mode), mode);
 }
 
 namespace {
@@ -283,7 +297,7 @@ int check_ffn_common(const moe_weights* w, int T, int k, const int32_t* slot_off
 }
 
 moe::GemvArgs gemv_args(const moe_weights* w, const void* x, int x_dtype, int T, int k,
-                        const int32_t* perm, const int32_t* off, float* y, void* ws) {
+                        const int32_t* perm, const int32_t* off, float* y, void* ws, int mode) {
   moe::GemvArgs g{};
   g.wdt = w->wdtype;
   g.xdt = x_dtype;
@@ -301,14 +315,14 @@ moe::GemvArgs gemv_args(const moe_weights* w, const void* x, int x_dtype, int T,
   g.x = x;
   g.perm = perm;
   g.off = off;
-  g.a = static_cast<float*>(carve_ffn(ws, w, T, k).a);
+  g.a = static_cast<float*>(carve_ffn(ws, w, T, k, mode).a);
   g.y = y;
   return g;
 }
 
 moe::GemmArgs gemm_args(const moe_weights* w, const void* x, int x_dtype, int T, int k,
-                        const int32_t* perm, const int32_t* off, float* y, void* ws) {
-  const FfnWs f = carve_ffn(ws, w, T, k);
+                        const int32_t* perm, const int32_t* off, float* y, void* ws, int mode) {
+  const FfnWs f = carve_ffn(ws, w, T, k, mode);
   moe::GemmArgs g{};
   g.wdt = w->wdtype;
   g.xdt = x_dtype;
@@ -330,6 +344,10 @@ moe::GemmArgs gemm_args(const moe_weights* w, const void* x, int x_dtype, int T,
   g.tiles_gu = f.tiles_gu;
   g.tiles_dn = f.tiles_dn;
   g.counts = f.counts;
+  g.xq = f.xq;
+  g.xs = f.xs;
+  g.aq = f.aq;
+  g.as = f.as;
   return g;
 }
 
@@ -343,15 +361,32 @@ int moe_expert_gate_up(const moe_weights* w, const void* x, int x_dtype, int T, 
   if (T > 0 && (!x || !perm)) return fail(MOE_ERR_INVALID_ARG, "x / perm is NULL");
   if (!aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned");
   if (T == 0) return MOE_OK;
-  if (resolve_path(path, T, k, w) == MOE_PATH_GEMM) {
-    moe::GemmArgs g = gemm_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws);
-    hipError_t e = moe::launch_gemm_schedule(g, as_stream(stream));
-    if (e == hipSuccess) e = moe::launch_gemm_gate_up(g, as_stream(stream));
+  hipStream_t st = as_stream(stream);
+  const int rp = resolve_path(path, T, k, w, mode);
+  const int R = T * k;
+  if (rp == MOE_PATH_GEMM) {
+    moe::GemmArgs g = gemm_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws, mode);
+    hipError_t e = hipSuccess;
+    if (mode == MOE_MODE_B)  // E4M3 codes + E8M0 scales of x
+      e = moe::launch_act_quant(x, x_dtype, T, w->H, nullptr, g.xq, g.xs, nullptr, 0, st);
+    if (e == hipSuccess) e = moe::launch_gemm_schedule(g, st);
+    if (e == hipSuccess) e = mode == MOE_MODE_B ? moe::launch_gemm_gate_up_q(g, st) : moe::launch_gemm_gate_up(g, st);
+    if (e == hipSuccess && mode == MOE_MODE_B)  // and of a (fp32), over the n_res resident rows
+      e = moe::launch_act_quant(g.a, MOE_F32, R, w->I, slot_offsets + w->S, g.aq, g.as, nullptr, 0, st);
     if (e != hipSuccess) return hip_fail(e, "gate/up GEMM");
     return MOE_OK;
   }
-  moe::GemvArgs g = gemv_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws);
-  hipError_t e = moe::launch_gemv_gate_up(g, as_stream(stream));
+  moe::GemvArgs g = gemv_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws, mode);
+  hipError_t e = hipSuccess;
+  if (mode == MOE_MODE_B) {  // x quantised and dequantised (exactly) into bf16
+    void* xb = carve_ffn(ws, w, T, k, mode).xb;
+    e = moe::launch_act_quant(x, x_dtype, T, w->H, nullptr, nullptr, nullptr, xb, MOE_BF16, st);
+    g.x = xb;
+    g.xdt = MOE_BF16;
+  }
+  if (e == hipSuccess) e = moe::launch_gemv_gate_up(g, st);
+  if (e == hipSuccess && mode == MOE_MODE_B)  // a quantised in place
+    e = moe::launch_act_quant(g.a, MOE_F32, R, w->I, slot_offsets + w->S, nullptr, nullptr, g.a, MOE_F32, st);
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMV");
   return MOE_OK;
 }
@@ -362,13 +397,13 @@ int moe_expert_down(const moe_weights* w, int T, int k, const int32_t* slot_offs
   if (T > 0 && !y_perm) return fail(MOE_ERR_INVALID_ARG, "y_perm is NULL");
   if (!aligned(y_perm, 16)) return fail(MOE_ERR_INVALID_ARG, "y_perm must be 16-byte aligned");
   if (T == 0) return MOE_OK;
-  if (resolve_path(path, T, k, w) == MOE_PATH_GEMM) {
-    moe::GemmArgs g = gemm_args(w, nullptr, MOE_BF16, T, k, nullptr, slot_offsets, y_perm, ws);
-    hipError_t e = moe::launch_gemm_down(g, as_stream(stream));
+  if (resolve_path(path, T, k, w, mode) == MOE_PATH_GEMM) {
+    moe::GemmArgs g = gemm_args(w, nullptr, MOE_BF16, T, k, nullptr, slot_offsets, y_perm, ws, mode);
+    hipError_t e = mode == MOE_MODE_B ? moe::launch_gemm_down_q(g, as_stream(stream)) : moe::launch_gemm_down(g, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, "down GEMM");
     return MOE_OK;
   }
-  moe::GemvArgs g = gemv_args(w, nullptr, MOE_F32, T, k, nullptr, slot_offsets, y_perm, ws);
+  moe::GemvArgs g = gemv_args(w, nullptr, MOE_F32, T, k, nullptr, slot_offsets, y_perm, ws, mode);
   hipError_t e = moe::launch_gemv_down(g, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "down GEMV");
   return MOE_OK;
@@ -481,7 +516,7 @@ struct LayerWs {
 };
 
 LayerWs carve_layer(void* ws, int T, const moe_routing* cfg, const moe_weights* w, int path,
-                    int with_rw) {
+                    int mode, int with_rw) {
   Carve c(ws);
   LayerWs L{};
   const size_t R = size_t(T) * cfg->k;
@@ -495,7 +530,7 @@ LayerWs carve_layer(void* ws, int T, const moe_routing* cfg, const moe_weights* 
   L.inv = c.take<int32_t>(R * 4);
   L.miss_count = c.take<int32_t>(4);
   L.y = c.take<float>(R * w->H * 4);
-  L.ffn = c.take<char>(ffn_ws_size(w, T, cfg->k, path));
+  L.ffn = c.take<char>(ffn_ws_size(w, T, cfg->k, path, mode));
   L.used = c.used;
   return L;
 }
@@ -503,9 +538,8 @@ LayerWs carve_layer(void* ws, int T, const moe_routing* cfg, const moe_weights* 
 
 size_t moe_layer_workspace_size(int T, const moe_routing* cfg, const moe_weights* w, int path,
                                 int mode, int with_router_weights) {
-  (void)mode;
   if (!cfg || !w || T < 0 || cfg->k < 1 || cfg->E < 1) return 0;
-  return carve_layer(nullptr, T, cfg, w, resolve_path(path, T, cfg->k, w), with_router_weights).used;
+  return carve_layer(nullptr, T, cfg, w, resolve_path(path, T, cfg->k, w, mode), mode, with_router_weights).used;
 }
 
 int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const float* logits,
@@ -532,21 +566,38 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
   if (!aligned(x, 16) || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "x / out must be 16-byte aligned");
   if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const int rp = resolve_path(path, T, cfg->k, w);
+  const int rp = resolve_path(path, T, cfg->k, w, mode);
   const int with_rw = w_router != nullptr;
   const size_t need = moe_layer_workspace_size(T, cfg, w, path, mode, with_rw);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
-  LayerWs L = carve_layer(ws, T, cfg, w, rp, with_rw);
+  LayerWs L = carve_layer(ws, T, cfg, w, rp, mode, with_rw);
   int32_t* tidx = topk_idx ? topk_idx : L.topk_idx;
   float* tw = topk_w ? topk_w : L.topk_w;
   MOE_TRY(moe_route_permute(x, x_dtype, T, w->H, w_router, logits, bias, cfg, slot_map, w->S, tidx, tw,
                             L.counts, L.offsets, L.perm, L.inv, miss_count ? miss_count : L.miss_count,
                             miss_token, miss_expert, miss_weight, L.rp, L.rp_bytes, stream));
   if (T == 0) return MOE_OK;
-  const size_t ffn_bytes = ffn_ws_size(w, T, cfg->k, rp);
+  const size_t ffn_bytes = ffn_ws_size(w, T, cfg->k, rp, mode);
   MOE_TRY(moe_expert_ffn(w, x, x_dtype, T, cfg->k, L.perm, L.offsets, rp, mode, L.y, L.ffn,
                          ffn_bytes, stream));
   return moe_combine(L.y, L.inv, tw, T, cfg->k, w->H, out, out_dtype, stream);
+}
+
+int moe_quantize_mx_e4m3(const void* in, int in_dtype, int rows, int K, uint8_t* codes, uint8_t* scales,
+                         void* deq, int deq_dtype, void* stream) {
+  MOE_TRY(check_act_dtype(in_dtype, "in"));
+  if (rows < 0 || K < 32 || K % 32) return fail(MOE_ERR_INVALID_ARG, "rows = %d, K = %d: K must be a positive multiple of 32", rows, K);
+  if ((long long)rows * K > (1LL << 40)) return fail(MOE_ERR_UNSUPPORTED, "rows * K too large");
+  if (deq) MOE_TRY(check_act_dtype(deq_dtype, "deq"));
+  if (deq && deq == in && !(in_dtype == MOE_F32 && deq_dtype == MOE_F32))
+    return fail(MOE_ERR_INVALID_ARG, "in-place quantisation needs fp32 in and out");
+  if (rows > 0 && (!in || (!codes && !scales && !deq))) return fail(MOE_ERR_INVALID_ARG, "a NULL pointer");
+  if (!aligned(in, 16) || !aligned(codes, 8) || !aligned(deq, 16))
+    return fail(MOE_ERR_INVALID_ARG, "in / deq must be 16-byte and codes 8-byte aligned");
+  if (rows == 0) return MOE_OK;
+  hipError_t e = moe::launch_act_quant(in, in_dtype, rows, K, nullptr, codes, scales, deq, deq_dtype, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantise");
+  return MOE_OK;
 }
 
 int moe_check_device_error(const void* ws, void* stream) {

@@ -21,7 +21,7 @@ ELEM_TOL = 2e-2
 L2_TOL = 5e-3
 
 
-def assert_fp_close(gpu, ref, what, elem_tol=ELEM_TOL, l2_tol=L2_TOL):
+def assert_fp_close(gpu, ref, what, elem_tol=ELEM_TOL, l2_tol=L2_TOL, scale_tol=ELEM_TOL):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
@@ -31,9 +31,9 @@ def assert_fp_close(gpu, ref, what, elem_tol=ELEM_TOL, l2_tol=L2_TOL):
     err = np.abs(gpu - ref)
     assert np.all(err <= elem_tol * np.maximum(1.0, np.abs(ref))), f"{what}: elementwise bound, max err {err.max()}"
     rms = np.sqrt(np.mean(ref ** 2))
-    bound = elem_tol * np.maximum(np.abs(ref), rms)
+    bound = scale_tol * np.maximum(np.abs(ref), rms)
     bad = err > bound
-    assert not bad.any(), f"{what}: {bad.sum()} elements beyond 2e-2*max(|ref|, rms); worst {(err / np.maximum(bound, 1e-300)).max():.3g}x"
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond {scale_tol:g}*max(|ref|, rms); worst {(err / np.maximum(bound, 1e-300)).max():.3g}x"
     nr = np.linalg.norm(ref)
     if nr > 0:
         rel = np.linalg.norm(gpu - ref) / nr

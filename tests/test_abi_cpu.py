@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -123,6 +123,22 @@ def test_expert_ffn_validation(L):
     _expect(moe.MOE_ERR_INVALID_ARG, call, slot_offsets=None)
     n = moe.moe_expert_ffn_workspace_size(w("bf16"), 4, 2, moe.MOE_PATH_GEMV, moe.MOE_MODE_A)
     assert n >= 4 * 2 * 128 * 4
+    # mode B: the matrix-core path only for FP8 / MXFP4 weights; one scale per 32 elements
+    _expect(moe.MOE_ERR_UNSUPPORTED, call, path=moe.MOE_PATH_GEMM, mode=moe.MOE_MODE_B)
+    _expect(moe.MOE_ERR_UNSUPPORTED, call, w=w("bf16", H=264), mode=moe.MOE_MODE_B)
+    _expect(moe.MOE_ERR_UNSUPPORTED, call, w=w("fp8", H=8192), path=moe.MOE_PATH_GEMM, mode=moe.MOE_MODE_B)
+    nb = moe.moe_expert_ffn_workspace_size(w("fp8"), 4, 2, moe.MOE_PATH_GEMM, moe.MOE_MODE_B)
+    na = moe.moe_expert_ffn_workspace_size(w("fp8"), 4, 2, moe.MOE_PATH_GEMM, moe.MOE_MODE_A)
+    assert nb >= na + 4 * 256 + 4 * 2 * 128  # quantised x and a with their scales
+
+
+def test_quantize_validation(L):
+    q = moe.moe_quantize_mx_e4m3
+    _expect(moe.MOE_ERR_INVALID_ARG, q, FAKE, moe.MOE_F32, 4, 48, FAKE, FAKE, None, moe.MOE_F32, 0)   # K % 32
+    _expect(moe.MOE_ERR_INVALID_ARG, q, FAKE, 7, 4, 64, FAKE, FAKE, None, moe.MOE_F32, 0)             # dtype
+    _expect(moe.MOE_ERR_INVALID_ARG, q, FAKE, moe.MOE_BF16, 4, 64, None, None, FAKE, moe.MOE_BF16, 0)  # in place, bf16
+    _expect(moe.MOE_ERR_INVALID_ARG, q, FAKE, moe.MOE_F32, 4, 64, None, None, None, moe.MOE_F32, 0)    # no output
+    _expect(moe.MOE_ERR_INVALID_ARG, q, FAKE + 4, moe.MOE_F32, 4, 64, FAKE, None, None, moe.MOE_F32, 0)  # alignment
 
 
 def test_combine_and_layer_validation(L):

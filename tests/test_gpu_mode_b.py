@@ -1,0 +1,142 @@
+"""GPU parity of mode B (activations quantised per row and 32 elements to E4M3 with an E8M0 scale
+before each projection) against the oracle with the same quantisation applied to its fp64
+activations.  The quantiser itself must agree with the oracle's bit for bit; the layer's outputs
+meet the usual floating-point bar.  The GEMM path runs on the block-scaled matrix cores (FP8 and
+MXFP4 weights), the GEMV path on the dequantised values (every weight format)."""
+import sys
+
+import numpy as np
+import pytest
+
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+# The block-scaled matrix cores do not accumulate a 64-wide product exactly in fp32 (sums of
+# E4M3 products that fp32 holds exactly come back with relative errors up to a few 1e-3), and the
+# second quantisation (of a, before down) turns such an error into a one-step E4M3 change of an
+# element now and then.  The stated bar (elementwise 2e-2*max(1,|ref|), relative L2 5e-3) holds;
+# the extra scale-aware elementwise bound is widened from 2e-2 to 8e-2 of max(|ref|, rms) on that
+# path only.
+GEMM_SCALE_TOL = 8e-2
+
+CASES = {
+    # K = 256 / 128: scale rows of 8 / 4 bytes (copied, not rotated), ragged groups
+    "fp8_zipf": gen.config("prefill_fp8_zipf", T=300, H=256, E=32, I=128, k=8),
+    # up rows straddling 128-row FP8 scale blocks, K = 384 / 320
+    "fp8_big_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=8, I=320, k=2),
+    # K = 1024 / 512: rotated scale rows loaded by direct loads; compact map with misses
+    "mxfp4_compact": gen.config("compact_mxfp4", T=256, H=1024, E=16, I=512, k=4, resident=11),
+    "mxfp4_ragged": gen.config("compact_mxfp4", T=200, H=512, E=24, I=192, k=6, resident=9),
+    # GEMV only
+    "bf16_decode": gen.config("decode_bf16", T=37, H=512, E=24, I=160, k=4),
+    "f32_tiny": gen.config("tiny", T=21, I=128),
+}
+
+
+def _gemm_ok(cfg):
+    return cfg.wdtype in ("fp8", "mxfp4") and cfg.H % 64 == 0 and cfg.I % 64 == 0
+
+
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def case(request):
+    _gpu()
+    from gpu_cases import GpuCase, run_oracle
+    from oracle import moe_oracle as O
+    cfg = CASES[request.param]
+    inp = gen.make_inputs(cfg)
+    return request.param, inp, GpuCase(inp), run_oracle(inp, act_quant=O.act_quant_mx_e4m3), run_oracle(inp)
+
+
+def _banner(what):
+    print(f"[gpu-mode-b] {what}", flush=True)
+    sys.stdout.flush()
+
+
+def test_quantizer_bit_exact():
+    _gpu()
+    import torch
+
+    import routed_expert_ffn_05_amd as moe
+    from oracle import moe_oracle as O
+    from routed_expert_ffn_05_amd import device as D
+    rng = np.random.default_rng(5)
+    rows, K = 67, 512
+    # per-block magnitudes over many binades, exact zeros, whole zero blocks, ties and values at
+    # and above the saturation point of a block
+    x = rng.standard_normal((rows, K)) * np.exp2(rng.integers(-30, 30, (rows, K // 32)))[:, :, None].repeat(32, 2).reshape(rows, K)
+    x[3, :32] = 0.0
+    x[5, 7] = 0.0
+    x[9, 32:64] = np.arange(32) * 0.125 - 2.0
+    x[11, :32] = 1.0
+    x[11, 0] = 511.0  # amax 511 -> X = 0; 448 < 480 < 511 saturate
+    x[11, 1] = 480.0
+    for dt in ("f32", "bf16"):
+        _banner(f"quantizer {dt}")
+        if dt == "f32":
+            xs = x.astype(np.float32)
+            x64 = xs.astype(np.float64)
+            d_x = D.to_device(xs)
+            xdt = moe.MOE_F32
+        else:
+            bits = gen.f32_to_bf16_bits(x.astype(np.float32))
+            x64 = O.bf16_to_f64(bits)
+            d_x = D.to_device(bits)
+            xdt = moe.MOE_BF16
+        ref = O.act_quant_mx_e4m3(x64)
+        codes = torch.empty((rows, K), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device="cuda")
+        deq = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+        deqb = torch.empty((rows, K), dtype=torch.int16, device="cuda")
+        moe.moe_quantize_mx_e4m3(d_x, xdt, rows, K, codes, scales, deq, moe.MOE_F32, 0)
+        moe.moe_quantize_mx_e4m3(d_x, xdt, rows, K, None, None, deqb, moe.MOE_BF16, 0)
+        torch.cuda.synchronize()
+        dq = deq.cpu().numpy().astype(np.float64)
+        assert np.array_equal(dq, ref), f"{dt}: {np.sum(dq != ref)} values differ"
+        dqb = O.bf16_to_f64(deqb.cpu().numpy().view(np.uint16))
+        assert np.array_equal(dqb, ref)
+        c = codes.cpu().numpy()
+        s = scales.cpu().numpy().astype(np.int64) - 127
+        val = O.e4m3fn_to_f64(c) * np.exp2(np.repeat(s, 32, axis=1))
+        assert np.array_equal(val, ref)
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+def test_mode_b_expert_ffn(case, path):
+    import routed_expert_ffn_05_amd as moe
+    from gpu_cases import assert_fp_close
+    name, inp, g, ref, plain = case
+    _banner(f"{name}/expert_ffn/{path}")
+    p = moe.MOE_PATH_GEMV if path == "gemv" else moe.MOE_PATH_GEMM
+    if path == "gemm" and not _gemm_ok(inp.cfg):
+        with pytest.raises(moe.MoeError) as ei:
+            g.expert_ffn(ref["perm"], ref["slot_offsets"], path=p, mode=moe.MOE_MODE_B)
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+        return
+    y = g.expert_ffn(ref["perm"], ref["slot_offsets"], path=p, mode=moe.MOE_MODE_B)
+    assert_fp_close(y, ref["y_perm"], f"{name} y_perm (mode B, {path})",
+                    scale_tol=GEMM_SCALE_TOL if path == "gemm" else 2e-2)
+    # information: mode B against the unquantised oracle
+    n = np.linalg.norm(plain["y_perm"])
+    if n > 0:
+        print(f"[gpu-mode-b] {name} {path}: mode B vs plain oracle relative L2 "
+              f"{np.linalg.norm(y - plain['y_perm']) / n:.3g}")
+
+
+def test_mode_b_layer(case):
+    import routed_expert_ffn_05_amd as moe
+    from gpu_cases import assert_fp_close, check_routing
+    name, inp, g, ref, plain = case
+    _banner(f"{name}/layer")
+    res = g.layer(mode=moe.MOE_MODE_B)
+    flipped = check_routing(res["topk_idx"], res["topk_w"], ref)
+    keep = np.array([t not in flipped for t in range(inp.cfg.T)], bool)
+    gemm = _gemm_ok(inp.cfg) and inp.cfg.T * inp.cfg.k > 4 * inp.cfg.S  # the path AUTO takes
+    assert_fp_close(res["out"][keep], ref["out"][keep], f"{name} layer out (mode B)",
+                    scale_tol=GEMM_SCALE_TOL if gemm else 2e-2)

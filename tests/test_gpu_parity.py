@@ -28,6 +28,9 @@ SMALL = {
     # more than 2048 rows: the permutation runs as several work-groups (ragged last group), with
     # compact misses
     "mxfp4_multigroup_perm": gen.config("compact_mxfp4", T=700, H=256, E=48, I=128, k=5, resident=17),
+    # down-projection rows of exactly 64 16-byte chunks (16 lanes per row, two rows per step)
+    "fp8_down64": gen.config("decode_fp8", T=29, H=256, E=20, I=1024, k=3),
+    "bf16_down64": gen.config("decode_bf16", T=6, H=256, E=12, I=512, k=2),
 }
 
 

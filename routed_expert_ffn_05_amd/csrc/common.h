@@ -119,6 +119,17 @@ __device__ __forceinline__ float wave_max_all(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Unsigned 32-bit maximum over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, uint32_t(dpp_src_or<0x111>(0, int(v))));
+  v = max(v, uint32_t(dpp_src_or<0x112>(0, int(v))));
+  v = max(v, uint32_t(dpp_src_or<0x114>(0, int(v))));
+  v = max(v, uint32_t(dpp_src_or<0x118>(0, int(v))));
+  v = max(v, uint32_t(dpp_src_or<0x142, 0xA>(0, int(v))));
+  v = max(v, uint32_t(dpp_src_or<0x143, 0xC>(0, int(v))));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+
 // Unsigned 64-bit maximum over the wave, returned to every lane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #define MOE_MAXU64_STEP(CTRL, RM)                                                        \

@@ -55,9 +55,16 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
     uint64_t best = key[0];
 #pragma unroll
     for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = int(~uint32_t(best));
-    const uint32_t h = uint32_t(best >> 32);
+    // the largest logit over the wave (high words); its lane, or among equal logits the smallest id
+    const uint32_t bh = uint32_t(best >> 32);
+    const uint32_t h = wave_max_u32(bh);
+    const unsigned long long tie = __ballot(bh == h);
+    int e;
+    if (__popcll(tie) == 1) {
+      e = int(~uint32_t(__builtin_amdgcn_readlane(int(uint32_t(best)), __ffsll((long long)tie) - 1)));
+    } else {
+      e = int(~wave_max_u32(bh == h ? uint32_t(best) : 0u));
+    }
     const float l = __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h);
     if ((e & 63) == lane) {
 #pragma unroll

@@ -177,3 +177,21 @@ def test_out_of_range_expert_sets_device_error():
     with pytest.raises(moe.MoeError) as ei:
         g.permute(idx, np.full((4, 2), 0.5, np.float32))
     assert ei.value.status == moe.MOE_ERR_DEVICE
+
+
+@pytest.mark.parametrize("T", [5, 40])
+def test_exact_ties_resolved_by_expert_id(T):
+    # logits on a coarse grid: many exactly equal values; given logits (no GEMV) reach both sides
+    # unchanged, so the (logit desc, id asc) order must agree on every token, ties included
+    _gpu()
+    from gpu_cases import GpuCase, run_oracle
+    cfg = gen.config("decode_fp8", T=T, H=256, E=200, I=128, k=8)
+    inp = gen.make_inputs(cfg)
+    rng = np.random.default_rng(77)
+    inp.logits = (rng.integers(0, 6, (T, cfg.E)) * 0.25).astype(np.float32)
+    _banner(f"ties/T{T}", cfg)
+    g = GpuCase(inp)
+    ref = run_oracle(inp)
+    res = g.route_permute()
+    assert np.array_equal(res["topk_idx"], ref["topk_idx"])
+    np.testing.assert_allclose(res["topk_w"], ref["topk_w"], rtol=1e-6)

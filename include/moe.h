@@ -69,7 +69,7 @@ typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 
  * fp32 accumulation.  MODE_B: the activations entering each projection (x before gate/up, a
  * before down) are quantised per row and per 32 K-elements as moe_quantize_mx_e4m3 does.  The
  * GEMM path then multiplies the E4M3 codes with the FP8 or MXFP4 weights on the block-scaled
- * matrix cores (FP8 or MXFP4 weights only, H and I multiples of 64 and at most 4096); the GEMV
+ * matrix cores (FP8 or MXFP4 weights only, H and I multiples of 128 and at most 4096); the GEMV
  * path (any weight dtype, H and I multiples of 32) multiplies the dequantised values, which are
  * exact in bf16/fp32.  Mode B is judged against the same quantisation applied in the reference
  * model of the layer. */

@@ -34,7 +34,7 @@
 namespace moe {
 namespace gemm {
 
-constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int BM = 128, BN = 256;
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
 constexpr int kMaxFp4Kb = 128;  // MXFP4: E8M0 scales per row staged in LDS (K <= 4096)
 
@@ -42,16 +42,22 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) const void lds_void;
 
-// B operand bytes per row and K step, direct loads per wave and step, LDS for the stages
+// K step, operand bytes per row and step, direct loads per wave and step, LDS for the stages.
+// The K step makes every weight row segment a whole 128-byte line where LDS allows (bf16: 64,
+// FP8: 128 elements; MXFP4: 128 elements = 64 bytes), since each direct load of a line segment
+// occupies one of the CU's outstanding-request slots whatever its length.
 template <int WD> struct BFmt {
-  static constexpr int ROW = WD == DT_BF16 ? 128 : WD == DT_FP8 ? 64 : 32;
+  static constexpr int BK = WD == DT_BF16 ? 64 : 128;
+  static constexpr int ROW = WD == DT_BF16 ? 128 : WD == DT_FP8 ? 128 : 64;  // B bytes per row
+  static constexpr int AROW = BK * 2;                                         // A (bf16) bytes per row
   static constexpr int STAGE = BN * ROW;
   static constexpr int INSTR = STAGE / (1024 * kWaves);
+  static constexpr int KS = BK / 16;  // MFMA sub-steps per step
   // the MXFP4 tile keeps its E8M0 scales (BN x K/32 bytes) in LDS beside the stages
   static constexpr int BUDGET = WD == DT_MXFP4 ? 112 * 1024 : 144 * 1024;
-  // a K step of a tile with NS row blocks occupies NS*4 KiB of A plus the B tile; as many steps
+  // a K step of a tile with NS row blocks occupies 32*NS A rows plus the B tile; as many steps
   // are kept in flight as the budget holds (at most 8)
-  static constexpr int stage_bytes(int ns) { return ns * 4096 + STAGE; }
+  static constexpr int stage_bytes(int ns) { return ns * 32 * AROW + STAGE; }
   static constexpr int nstage(int ns) { return BUDGET / stage_bytes(ns) < 8 ? BUDGET / stage_bytes(ns) : 8; }
 };
 
@@ -76,7 +82,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(uint32_t(size_t((lds_void*)p)));
 }
 
-// swizzled position of 16-byte granule g in a row r of a 128-byte (bf16) tile row
+// swizzled position of 16-byte granule g in row r of a 256-byte tile row (16 granules)
+__device__ __forceinline__ int swz256(int r, int g) { return g ^ (r & 15); }
+// 128-byte rows
 __device__ __forceinline__ int swz128(int r, int g) { return g ^ ((r >> 1) & 7); }
 // 64-byte rows (fp8)
 __device__ __forceinline__ int swz64(int r, int g) { return g ^ ((r >> 2) & 3); }
@@ -133,10 +141,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   // rows past N read the last row (valid memory; their columns are never stored)
   auto brow_clamped = [&](int r) -> int { return min(brow_global(r), N - 1); };
 
+  constexpr int BK = F::BK;
+  // swizzled slot of A granule g in tile row r
+  auto swzA = [](int r, int g) -> int {
+    if constexpr (F::AROW == 256) return swz256(r, g);
+    return swz128(r, g);
+  };
+  constexpr int AGR = F::AROW / 16;     // A granules per row
+  constexpr int ARPC = 1024 / F::AROW;  // A rows per 1 KiB chunk
+
   // ---- per-lane sources of the direct loads ---------------------------------------------------
   // A (set up per row-block count in run()): with NS row blocks the tile's first 32*NS rows are
-  // loaded as 4*NS chunks of 8 rows x 128 bytes; chunk c is issued by wave c % 8, lane -> row
-  // 8c + lane/8, slot lane%8.  Rows past the tile read a valid row and are never stored.
+  // loaded as 1 KiB chunks of ARPC rows; chunk c is issued by wave c % 8, lane -> row
+  // ARPC*c + lane/AGR, slot lane%AGR.  Rows past the tile read a valid row and are never stored.
   auto a_source = [&](int r) -> const uint8_t* {
     int src = GATEUP ? 0 : m0;
     if (r < rows) {
@@ -147,24 +164,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         src = m0 + r;
       }
     }
-    return reinterpret_cast<const uint8_t*>(act + size_t(src) * K) + swz128(r, lane & 7) * 16;
+    return reinterpret_cast<const uint8_t*>(act + size_t(src) * K) + swzA(r, lane % AGR) * 16;
   };
-  // B: chunk c = INSTR*w + j covers 1 KiB of the tile: 128-byte rows like A (bf16); 64-byte rows:
-  // lane -> row 16c + lane/4 (fp8); 32-byte rows: lane -> row 32c + lane/2 (fp4)
+  // B: chunk c = INSTR*w + j covers 1 KiB of the tile: 128-byte rows, lane -> row 8c + lane/8
+  // (bf16, FP8); 64-byte rows: lane -> row 16c + lane/4 (MXFP4)
   const uint8_t* bsrc[F::INSTR];
 #pragma unroll
   for (int j = 0; j < F::INSTR; ++j) {
     const int c = F::INSTR * wv + j;
     int r, g;
-    if constexpr (WD == DT_BF16) {
+    if constexpr (F::ROW == 128) {
       r = 8 * c + (lane >> 3);
       g = swz128(r, lane & 7);
-    } else if constexpr (WD == DT_FP8) {
+    } else {
       r = 16 * c + (lane >> 2);
       g = swz64(r, lane & 3);
-    } else {
-      r = 32 * c + (lane >> 1);
-      g = swz32(r, lane & 1);
     }
     bsrc[j] = wslot + size_t(brow_clamped(r)) * rb + g * 16;
   }
@@ -229,22 +243,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
   auto run = [&](auto ns_c) {
     constexpr int NS = decltype(ns_c)::value;
-    constexpr int NA = 4 * NS;                        // A chunks per step
+    constexpr int AB = NS * 32 * F::AROW;             // A bytes per stage
+    constexpr int NA = AB / 1024;                     // A chunks per step
     constexpr int A_HI = (NA + kWaves - 1) / kWaves;  // A chunks of waves 0 .. NA%8-1 (or all)
     constexpr int A_LO = NA / kWaves;                 // A chunks of the other waves
     constexpr int NST = F::nstage(NS);                // K steps in flight
     constexpr int SB = F::stage_bytes(NS);            // bytes per stage: A rows, then the B tile
-    constexpr int AB = NS * 4096;
-    constexpr int KS = BK / 16;                       // MFMA K sub-steps per step
+    constexpr int KS = F::KS;                         // MFMA K sub-steps per step
     constexpr int kReads = NS + (WD == DT_MXFP4 ? 2 : 1);  // LDS reads per sub-step
-    static_assert(NST >= 3, "LDS budget");
+    static_assert(NST >= 2, "LDS budget");
     const int na = (NA % kWaves == 0 || wv < NA % kWaves) ? A_HI : A_LO;  // this wave's A chunks
     const int nl = na + F::INSTR;                                       // its loads per step
     const uint8_t* asrc[A_HI];
 #pragma unroll
     for (int j = 0; j < A_HI; ++j) {
       const int c = j < na ? wv + kWaves * j : wv;  // unused entries point at a valid row
-      asrc[j] = a_source(8 * c + (lane >> 3));
+      asrc[j] = a_source(ARPC * c + lane / AGR);
     }
     const uint32_t lds0 = lds_addr(smem);
     // direct load j of this wave for K step kk into the stage at LDS address st: j < na are
@@ -283,18 +297,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 #pragma unroll
       for (int ms = 0; ms < NS; ++ms) {
         const int m = ms * 32 + ln;
-        f.a[ms] = *reinterpret_cast<const bf16x8_t*>(st + m * 128 + swz128(m, ks * 2 + kh) * 16);
+        f.a[ms] = *reinterpret_cast<const bf16x8_t*>(st + m * F::AROW + swzA(m, ks * 2 + kh) * 16);
       }
       const uint8_t* B = st + AB;
       if constexpr (WD == DT_BF16) {
         const uint4 q = *reinterpret_cast<const uint4*>(B + bl * 128 + swz128(bl, ks * 2 + kh) * 16);
         f.b[0] = q.x; f.b[1] = q.y; f.b[2] = q.z; f.b[3] = q.w;
-      } else if constexpr (WD == DT_FP8) {
-        const uint2 q = *reinterpret_cast<const uint2*>(B + bl * 64 + swz64(bl, ks) * 16 + kh * 8);
+      } else if constexpr (WD == DT_FP8) {  // 128 K per row: granule ks holds K [16ks, 16ks+16)
+        const uint2 q = *reinterpret_cast<const uint2*>(B + bl * 128 + swz128(bl, ks) * 16 + kh * 8);
         f.b[0] = q.x; f.b[1] = q.y;
-      } else {
-        f.b[0] = *reinterpret_cast<const uint32_t*>(B + bl * 32 + swz32(bl, ks >> 1) * 16 + (ks & 1) * 8 + kh * 4);
-        const int kb = kk * 2 + (ks >> 1);
+      } else {  // 64-byte rows of 128 K: granule ks/2 holds K [32(ks/2), +32)
+        f.b[0] = *reinterpret_cast<const uint32_t*>(B + bl * 64 + swz64(bl, ks >> 1) * 16 + (ks & 1) * 8 + kh * 4);
+        const int kb = kk * (BK / 32) + (ks >> 1);
         if (fp4_async) {
           int slot = (kb >> 4) + fp4_keyl;
           slot -= slot >= gpr ? gpr : 0;
@@ -378,17 +392,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
       }
       if constexpr (kBlockScaled) {
-        // end of a 128-wide K block (or of K): fold the block's partial sums in with their scale
-        if (((kk + 1) * BK) % 128 == 0 || kk + 1 == nk) {
-          const float sc = Ssc[srow][(kk * BK) >> 7];
+        // a step is one 128-wide K block: fold its partial sums in with the block's scale
+        const float sc = Ssc[srow][kk];
 #pragma unroll
-          for (int ms = 0; ms < NS; ++ms)
+        for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              acc[ms][r] = fmaf(sc, tmp[ms][r], acc[ms][r]);
-              tmp[ms][r] = 0.0f;
-            }
-        }
+          for (int r = 0; r < 16; ++r) {
+            acc[ms][r] = fmaf(sc, tmp[ms][r], acc[ms][r]);
+            tmp[ms][r] = 0.0f;
+          }
       }
     }
     wait_vmcnt<0>();  // the trailing re-loads must land before the work-group's LDS is released
@@ -434,11 +446,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 // GATEUP = false: A = quantised a rows (positions),    out y (fp32)
 // ---------------------------------------------------------------------------------------------
 template <int WD> struct QFmt {
-  static constexpr int ROW = WD == DT_FP8 ? 64 : 32;        // B bytes per row and K step
+  static constexpr int BK = 128;                            // K step: 128-byte E4M3 rows
+  static constexpr int ROW = WD == DT_FP8 ? 128 : 64;       // B bytes per row and K step
   static constexpr int STAGE = BN * ROW;
   static constexpr int INSTR = STAGE / (1024 * kWaves);
   static constexpr int BUDGET = WD == DT_MXFP4 ? 104 * 1024 : 128 * 1024;
-  static constexpr int stage_bytes(int ns) { return ns * 2048 + STAGE; }  // A: 32*NS rows x 64 B
+  static constexpr int stage_bytes(int ns) { return ns * 4096 + STAGE; }  // A: 32*NS rows x 128 B
   static constexpr int nstage(int ns) { return BUDGET / stage_bytes(ns) < 8 ? BUDGET / stage_bytes(ns) : 8; }
 };
 
@@ -490,18 +503,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
     }
     return src;
   };
-  // B sources: 64-byte rows: lane -> row 16c + lane/4 (fp8); 32-byte rows: row 32c + lane/2 (fp4)
+  constexpr int BK = F::BK;
+  // B sources: 128-byte rows: lane -> row 8c + lane/8 (fp8); 64-byte rows: row 16c + lane/4 (fp4)
   const uint8_t* bsrc[F::INSTR];
 #pragma unroll
   for (int j = 0; j < F::INSTR; ++j) {
     const int c = F::INSTR * wv + j;
     int r, g;
     if constexpr (WD == DT_FP8) {
+      r = 8 * c + (lane >> 3);
+      g = swz128(r, lane & 7);
+    } else {
       r = 16 * c + (lane >> 2);
       g = swz64(r, lane & 3);
-    } else {
-      r = 32 * c + (lane >> 1);
-      g = swz32(r, lane & 1);
     }
     bsrc[j] = wslot + size_t(brow_clamped(r)) * rb + g * 16;
   }
@@ -566,21 +580,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
 
   auto run = [&](auto ns_c) {
     constexpr int NS = decltype(ns_c)::value;
-    constexpr int NA = 2 * NS;                        // A chunks (16 rows x 64 B) per step
+    constexpr int NA = 4 * NS;                        // A chunks (8 rows x 128 B) per step
     constexpr int A_HI = (NA + kWaves - 1) / kWaves;
     constexpr int A_LO = NA / kWaves;
     constexpr int NST = F::nstage(NS);
     constexpr int SB = F::stage_bytes(NS);
-    constexpr int AB = NS * 2048;
-    static_assert(NST >= 3, "LDS budget");
+    constexpr int AB = NS * 4096;
+    static_assert(NST >= 2, "LDS budget");
     const int na = (NA % kWaves == 0 || wv < NA % kWaves) ? A_HI : A_LO;
     const int nl = na + F::INSTR;
     const uint8_t* asrc[A_HI > 0 ? A_HI : 1];
 #pragma unroll
     for (int j = 0; j < (A_HI > 0 ? A_HI : 1); ++j) {
       const int c = j < na ? wv + kWaves * j : 0;
-      const int r = 16 * c + (lane >> 2);
-      asrc[j] = aq + size_t(a_row(r)) * K + swz64(r, lane & 3) * 16;
+      const int r = 8 * c + (lane >> 3);
+      asrc[j] = aq + size_t(a_row(r)) * K + swz128(r, lane & 7) * 16;
     }
     const uint32_t lds0 = lds_addr(smem);
     auto issue_one = [&](int j, int kk, uint32_t st) {
@@ -640,51 +654,55 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
       const int kn = min(kk + NST - 1, nk - 1);
       sr = sr + 1 == NST ? 0 : sr + 1;
       sw = sw + 1 == NST ? 0 : sw + 1;
-      // operands of this step: B (column bl), then per row block A and its scale
-      i32x8_t b;
-      const uint8_t* B = st + AB;
-      int sb = 127;
-      if constexpr (WD == DT_FP8) {
-        const uint4 q0 = *reinterpret_cast<const uint4*>(B + bl * 64 + swz64(bl, kh) * 16);
-        const uint4 q1 = *reinterpret_cast<const uint4*>(B + bl * 64 + swz64(bl, 2 + kh) * 16);
-        b[0] = q0.x; b[1] = q0.y; b[2] = q0.z; b[3] = q0.w;
-        b[4] = q1.x; b[5] = q1.y; b[6] = q1.z; b[7] = q1.w;
-      } else {
-        const uint4 q0 = *reinterpret_cast<const uint4*>(B + bl * 32 + swz32(bl, kh) * 16);
-        b[0] = q0.x; b[1] = q0.y; b[2] = q0.z; b[3] = q0.w;
-        b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
-        sb = Sfp4[sc_index(bl, kk * 2 + kh)];
-      }
-      i32x8_t a[NS];
-      int sa[NS];
-#pragma unroll
-      for (int ms = 0; ms < NS; ++ms) {
-        const int m = ms * 32 + ln;
-        const uint4 q0 = *reinterpret_cast<const uint4*>(st + m * 64 + swz64(m, kh) * 16);
-        const uint4 q1 = *reinterpret_cast<const uint4*>(st + m * 64 + swz64(m, 2 + kh) * 16);
-        a[ms][0] = q0.x; a[ms][1] = q0.y; a[ms][2] = q0.z; a[ms][3] = q0.w;
-        a[ms][4] = q1.x; a[ms][5] = q1.y; a[ms][6] = q1.z; a[ms][7] = q1.w;
-        sa[ms] = Sact[sc_index(m, kk * 2 + kh)];
-      }
       issue_step(kn, wst);
+      // two 64-wide MFMA sub-steps: lane (r, h) takes 8-bit granules 4s+h and 4s+2+h of its
+      // 128-byte row, or the 4-bit granule 2s+h of a 64-byte weight row; scales of K block
+      // 4kk + 2s + h
+      const uint8_t* B = st + AB;
 #pragma unroll
-      for (int ms = 0; ms < NS; ++ms) {
-        if constexpr (WD == DT_FP8)
-          tmp[ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ms], b, tmp[ms], 0, 0, 0, sa[ms], 0, sb);
-        else
-          acc[ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ms], b, acc[ms], 0, 4, 0, sa[ms], 0, sb);
-      }
-      if constexpr (WD == DT_FP8) {
-        if (((kk + 1) * BK) % 128 == 0 || kk + 1 == nk) {
-          const float sc = Ssc[srow][(kk * BK) >> 7];
-#pragma unroll
-          for (int ms = 0; ms < NS; ++ms)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              acc[ms][r] = fmaf(sc, tmp[ms][r], acc[ms][r]);
-              tmp[ms][r] = 0.0f;
-            }
+      for (int sub = 0; sub < 2; ++sub) {
+        const int kb = kk * 4 + 2 * sub + kh;
+        i32x8_t b;
+        int sb = 127;
+        if constexpr (WD == DT_FP8) {
+          const uint4 q0 = *reinterpret_cast<const uint4*>(B + bl * 128 + swz128(bl, 4 * sub + kh) * 16);
+          const uint4 q1 = *reinterpret_cast<const uint4*>(B + bl * 128 + swz128(bl, 4 * sub + 2 + kh) * 16);
+          b[0] = q0.x; b[1] = q0.y; b[2] = q0.z; b[3] = q0.w;
+          b[4] = q1.x; b[5] = q1.y; b[6] = q1.z; b[7] = q1.w;
+        } else {
+          const uint4 q0 = *reinterpret_cast<const uint4*>(B + bl * 64 + swz64(bl, 2 * sub + kh) * 16);
+          b[0] = q0.x; b[1] = q0.y; b[2] = q0.z; b[3] = q0.w;
+          b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+          sb = Sfp4[sc_index(bl, kb)];
         }
+        i32x8_t a[NS];
+        int sa[NS];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) {
+          const int m = ms * 32 + ln;
+          const uint4 q0 = *reinterpret_cast<const uint4*>(st + m * 128 + swz128(m, 4 * sub + kh) * 16);
+          const uint4 q1 = *reinterpret_cast<const uint4*>(st + m * 128 + swz128(m, 4 * sub + 2 + kh) * 16);
+          a[ms][0] = q0.x; a[ms][1] = q0.y; a[ms][2] = q0.z; a[ms][3] = q0.w;
+          a[ms][4] = q1.x; a[ms][5] = q1.y; a[ms][6] = q1.z; a[ms][7] = q1.w;
+          sa[ms] = Sact[sc_index(m, kb)];
+        }
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) {
+          if constexpr (WD == DT_FP8)
+            tmp[ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ms], b, tmp[ms], 0, 0, 0, sa[ms], 0, sb);
+          else
+            acc[ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ms], b, acc[ms], 0, 4, 0, sa[ms], 0, sb);
+        }
+      }
+      if constexpr (WD == DT_FP8) {  // a step is one 128-wide K block
+        const float sc = Ssc[srow][kk];
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[ms][r] = fmaf(sc, tmp[ms][r], acc[ms][r]);
+            tmp[ms][r] = 0.0f;
+          }
       }
     }
     wait_vmcnt<0>();

@@ -93,11 +93,15 @@ int check_weights(const moe_weights* w) {
   return MOE_OK;
 }
 
-// The matrix-core path needs K steps of 64 and, where E8M0 scale rows are staged in LDS (MXFP4
-// weights, mode B activations), K <= 4096.  Mode A decodes weights to bf16 exactly (bf16, FP8 or
-// MXFP4 weights); mode B multiplies E4M3 activations with FP8 or MXFP4 weights.
+// The matrix-core path needs whole K steps (64 elements for bf16 weights, 128 for FP8 and MXFP4
+// weights and for mode B, where E4M3 activation rows are 128-byte lines) and, where E8M0 scale
+// rows are staged in LDS (MXFP4 weights, mode B activations), K <= 4096.  Mode A decodes weights
+// to bf16 exactly (bf16, FP8 or MXFP4 weights); mode B multiplies E4M3 activations with FP8 or
+// MXFP4 weights.
 bool gemm_capable(const moe_weights* w, int mode) {
-  if (w->wdtype == MOE_F32 || w->H % 64 || w->I % 64) return false;
+  if (w->wdtype == MOE_F32) return false;
+  const int step = (w->wdtype == MOE_BF16 && mode == MOE_MODE_A) ? 64 : 128;
+  if (w->H % step || w->I % step) return false;
   const bool small_k = w->H <= 4096 && w->I <= 4096;
   if (mode == MOE_MODE_B) return (w->wdtype == MOE_FP8_E4M3_B128 || w->wdtype == MOE_MXFP4) && small_k;
   if (w->wdtype == MOE_MXFP4 && !small_k) return false;
@@ -120,9 +124,9 @@ int check_path_mode(int path, int mode, const moe_weights* w) {
     return fail(MOE_ERR_UNSUPPORTED, "mode B needs H and I multiples of 32 (one E8M0 scale per 32 elements)");
   if (path == MOE_PATH_GEMM && !gemm_capable(w, mode))
     return fail(MOE_ERR_UNSUPPORTED, mode == MOE_MODE_B
-                                         ? "the mode-B GEMM path needs FP8 or MXFP4 weights, H and I multiples of 64, at most 4096"
-                                         : "the GEMM path needs bf16, FP8 or MXFP4 weights, H and I multiples of 64 "
-                                           "(and at most 4096 for MXFP4)");
+                                         ? "the mode-B GEMM path needs FP8 or MXFP4 weights, H and I multiples of 128, at most 4096"
+                                         : "the GEMM path needs bf16 (H, I multiples of 64), FP8 or MXFP4 weights (H, I "
+                                           "multiples of 128; at most 4096 for MXFP4)");
   return MOE_OK;
 }
 

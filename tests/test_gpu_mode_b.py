@@ -28,6 +28,8 @@ CASES = {
     # K = 1024 / 512: rotated scale rows loaded by direct loads; compact map with misses
     "mxfp4_compact": gen.config("compact_mxfp4", T=256, H=1024, E=16, I=512, k=4, resident=11),
     "mxfp4_ragged": gen.config("compact_mxfp4", T=200, H=512, E=24, I=192, k=6, resident=9),
+    # several M tiles per slot on the block-scaled matrix cores
+    "fp8_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=4, I=256, k=2),
     # GEMV only
     "bf16_decode": gen.config("decode_bf16", T=37, H=512, E=24, I=160, k=4),
     "f32_tiny": gen.config("tiny", T=21, I=128),
@@ -35,7 +37,7 @@ CASES = {
 
 
 def _gemm_ok(cfg):
-    return cfg.wdtype in ("fp8", "mxfp4") and cfg.H % 64 == 0 and cfg.I % 64 == 0
+    return cfg.wdtype in ("fp8", "mxfp4") and cfg.H % 128 == 0 and cfg.I % 128 == 0
 
 
 def _gpu():

@@ -25,6 +25,9 @@ SMALL = {
     "bf16_gemm": gen.config("decode_bf16", T=70, H=512, E=12, I=192, k=4),
     "fp8_big_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=8, I=320, k=2),
     "mxfp4_gemm_compact": gen.config("compact_mxfp4", T=200, H=512, E=24, I=192, k=6, resident=9),
+    # the matrix-core path with FP8 / MXFP4 weights (K multiples of 128): several M tiles per slot
+    "fp8_gemm_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=4, I=256, k=2),
+    "mxfp4_gemm_groups": gen.config("compact_mxfp4", T=300, H=512, E=12, I=256, k=4, resident=5),
     # more than 2048 rows: the permutation runs as several work-groups (ragged last group), with
     # compact misses
     "mxfp4_multigroup_perm": gen.config("compact_mxfp4", T=700, H=256, E=48, I=128, k=5, resident=17),
@@ -35,7 +38,8 @@ SMALL = {
 
 
 def _gemm_capable(cfg):
-    return cfg.wdtype != "f32" and cfg.H % 64 == 0 and cfg.I % 64 == 0
+    step = 64 if cfg.wdtype == "bf16" else 128
+    return cfg.wdtype != "f32" and cfg.H % step == 0 and cfg.I % step == 0
 
 
 def _gpu():

@@ -62,7 +62,11 @@ typedef enum moe_dtype {
 
 typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 
-/* Expert-FFN implementation: AUTO picks GEMV when few rows share a slot (T*k <= 4*S). */
+/* Expert-FFN implementation.  GEMV streams each touched slot's weights once per group of rows
+ * (any weight dtype).  GEMM runs 128-row tiles on the matrix cores and needs bf16 weights with H
+ * and I multiples of 64, or FP8 / MXFP4 weights with H and I multiples of 128 (MXFP4: at most
+ * 4096); see moe_mode for mode B.  AUTO picks GEMM when it is available and T*k > 4*S, else
+ * GEMV.  Asking for GEMM where it is not available fails with MOE_ERR_UNSUPPORTED. */
 typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 } moe_path;
 
 /* Expert-FFN arithmetic.  MODE_A: activations kept in bf16/fp32, weights decoded exactly,

@@ -13,6 +13,12 @@
 // For small batches the top-k of every token runs in the same work-group first (one wave per
 // token), its results kept in LDS, so routing and permutation cost one launch.
 //
+// Batches of at most kSmallPermRows rows skip the counters: every row's composite key
+// (key << 16 | r) goes into an LDS table, and after one barrier each output is a count over that
+// table, read by LDS broadcast: a row's position is the number of rows with a smaller composite
+// key, a slot's offset the number of resident rows in smaller slots, an expert's count the number
+// of rows that chose it.
+//
 // Large batches (more than kPermOneGroupRows rows) spread the same three steps over work-groups
 // of 1024 rows each: (1) every group counts its rows per key and per expert into a global table,
 // (2) one group sums the table, scans the slot totals and turns each group's counts into its base
@@ -27,11 +33,15 @@ namespace moe {
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kPermOneGroupRows = 2048;  // larger batches use the multi-group kernels
+constexpr int kSmallPermRows = 128;      // batches up to this size rank rows by direct counts
 
 // LDS words used by permute_body
 __host__ __device__ inline size_t permute_lds_words(int E, int S) {
   return size_t(kPermWaves) * (S + 1) + E + (S + 2);
 }
+
+// LDS words used by permute_small_body
+__host__ __device__ inline size_t permute_small_lds_words(int R) { return size_t(2) * ((R + 3) & ~3); }
 
 // key of a row: slot, S for a miss, -1 for an invalid row (expert or slot out of range)
 __device__ __forceinline__ int row_key(const int32_t* topk_idx, int E, const int32_t* __restrict__ slot_map,
@@ -183,13 +193,105 @@ __device__ void permute_body(const int32_t* topk_idx, const float* topk_w, int T
   }
 }
 
+// The permutation of at most kSmallPermRows rows (see the file comment).  Thread roles: row tid
+// (tid < R), slot s = tid (and s = tid + 1024 for S = 1024), expert e = tid ^ 512 (E <= 1024), so
+// the row, slot and expert counts run in different waves.
+__device__ void permute_small_body(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
+                                   const int32_t* __restrict__ slot_map, int S, int32_t* __restrict__ counts,
+                                   int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm,
+                                   int32_t* __restrict__ inv_perm, int32_t* __restrict__ miss_count,
+                                   int32_t* __restrict__ miss_token, int32_t* __restrict__ miss_expert,
+                                   float* __restrict__ miss_weight, uint32_t* __restrict__ err, int32_t* lds) {
+  const int R = T * k, R4 = (R + 3) & ~3, n4 = R4 / 4;
+  uint32_t* ck = reinterpret_cast<uint32_t*>(lds);  // [R4] composite keys; ~0: invalid row or padding
+  int32_t* se = lds + R4;                           // [R4] expert of the row; -1: invalid or padding
+  const int tid = threadIdx.x;
+  if (tid < R4) {
+    uint32_t c = ~0u;
+    int e = -1;
+    if (tid < R) {
+      int ee;
+      const int key = row_key(topk_idx, E, slot_map, S, tid, ee);
+      if (key >= 0) {
+        c = (uint32_t(key) << 16) | uint32_t(tid);
+        e = ee;
+      }
+    }
+    ck[tid] = c;
+    se[tid] = e;
+  }
+  __syncthreads();
+  const uint4* ck4 = reinterpret_cast<const uint4*>(ck);
+  const int4* se4 = reinterpret_cast<const int4*>(se);
+  const uint32_t res_end = uint32_t(S) << 16;  // composite keys below this are resident rows
+  if (tid < R) {
+    const uint32_t c = ck[tid];
+    int pos = 0, n_res = 0;
+    for (int q = 0; q < n4; ++q) {
+      const uint4 v = ck4[q];
+      pos += int(v.x < c) + int(v.y < c) + int(v.z < c) + int(v.w < c);
+      n_res += int(v.x < res_end) + int(v.y < res_end) + int(v.z < res_end) + int(v.w < res_end);
+    }
+    if (c == ~0u) {
+      inv_perm[tid] = -1;
+    } else if (c < res_end) {
+      perm[pos] = tid;
+      inv_perm[tid] = pos;
+    } else {
+      const int m = pos - n_res;  // misses follow every resident row in (key, r) order
+      inv_perm[tid] = -1;
+      miss_token[m] = tid / k;
+      miss_expert[m] = se[tid];
+      miss_weight[m] = topk_w[tid];
+    }
+  }
+  for (int sl = tid; sl <= S; sl += kPermThreads) {
+    const uint32_t lo = uint32_t(sl) << 16;
+    int off = 0, below_next = 0, bad = 0;
+    for (int q = 0; q < n4; ++q) {
+      const uint4 v = ck4[q];
+      off += int(v.x < lo) + int(v.y < lo) + int(v.z < lo) + int(v.w < lo);
+      if (sl == S) {
+        const uint32_t hi = lo + 0x10000u;
+        below_next += int(v.x < hi) + int(v.y < hi) + int(v.z < hi) + int(v.w < hi);
+        bad += int(v.x == ~0u) + int(v.y == ~0u) + int(v.z == ~0u) + int(v.w == ~0u);
+      }
+    }
+    slot_offsets[sl] = off;
+    if (sl == S) {
+      if (miss_count) miss_count[0] = below_next - off;
+      err[0] = bad > R4 - R ? 1u : 0u;
+    }
+  }
+  const int e = tid ^ (kPermThreads / 2);
+  if (e < E) {
+    int n = 0;
+    for (int q = 0; q < n4; ++q) {
+      const int4 v = se4[q];
+      n += int(v.x == e) + int(v.y == e) + int(v.z == e) + int(v.w == e);
+    }
+    counts[e] = n;
+  }
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_small_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int k, int E,
+    const int32_t* __restrict__ slot_map, int S, int32_t* __restrict__ counts,
+    int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ miss_count, int32_t* __restrict__ miss_token,
+    int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight, uint32_t* __restrict__ err) {
+  extern __shared__ __align__(16) int32_t lds[];
+  permute_small_body(topk_idx, topk_w, T, k, E, slot_map, S, counts, slot_offsets, perm, inv_perm,
+                     miss_count, miss_token, miss_expert, miss_weight, err, lds);
+}
+
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int k, int E,
     const int32_t* __restrict__ slot_map, int S, int32_t* __restrict__ counts,
     int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     int32_t* __restrict__ miss_count, int32_t* __restrict__ miss_token,
     int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight, uint32_t* __restrict__ err) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ __align__(16) int32_t lds[];
   permute_body(topk_idx, topk_w, T, k, E, slot_map, S, counts, slot_offsets, perm, inv_perm,
                miss_count, miss_token, miss_expert, miss_weight, err, lds);
 }
@@ -203,11 +305,11 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
     int32_t* __restrict__ slot_offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     int32_t* __restrict__ miss_count, int32_t* __restrict__ miss_token,
     int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight, uint32_t* __restrict__ err) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ __align__(16) int32_t lds[];
   const int R = T * k;
   int32_t* sidx = lds;                                   // [R]
   float* sw = reinterpret_cast<float*>(lds + R);         // [R]
-  int32_t* scratch = lds + 2 * R;
+  int32_t* scratch = lds + ((2 * R + 3) & ~3);  // 16-byte aligned: the small path reads it 4 words at a time
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   for (int t = wid; t < T; t += kPermWaves) {
     int my_e;
@@ -221,8 +323,12 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_kernel(
     }
   }
   __syncthreads();
-  permute_body(sidx, sw, T, k, E, slot_map, S, counts, slot_offsets, perm, inv_perm, miss_count,
-               miss_token, miss_expert, miss_weight, err, scratch);
+  if (R <= kSmallPermRows)
+    permute_small_body(sidx, sw, T, k, E, slot_map, S, counts, slot_offsets, perm, inv_perm, miss_count,
+                       miss_token, miss_expert, miss_weight, err, scratch);
+  else
+    permute_body(sidx, sw, T, k, E, slot_map, S, counts, slot_offsets, perm, inv_perm, miss_count,
+                 miss_token, miss_expert, miss_weight, err, scratch);
 }
 
 static hipError_t set_lds(const void* kern, size_t lds) {
@@ -238,7 +344,7 @@ __host__ __device__ inline int perm_table_stride(int E, int S) { return S + 1 + 
 __global__ __launch_bounds__(kPermThreads) void perm_count_kernel(const int32_t* __restrict__ topk_idx, int R,
                                                                   int E, const int32_t* __restrict__ slot_map,
                                                                   int S, int32_t* __restrict__ table) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ __align__(16) int32_t lds[];
   const int K1 = S + 1, stride = perm_table_stride(E, S);
   int32_t* cnt = lds;        // [K1]
   int32_t* ecnt = lds + K1;  // [E]
@@ -376,7 +482,8 @@ size_t permute_scratch_bytes(int T, int k, int E, int S) {
 size_t permute_lds_bytes(int E, int S) { return sizeof(int32_t) * permute_lds_words(E, S); }
 
 size_t route_permute_lds_bytes(int T, int k, int E, int S) {
-  return sizeof(int32_t) * (size_t(2) * T * k + permute_lds_words(E, S));
+  const int R = T * k;
+  return sizeof(int32_t) * (size_t((2 * R + 3) & ~3) + (R <= kSmallPermRows ? permute_small_lds_words(R) : permute_lds_words(E, S)));
 }
 
 hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
@@ -398,6 +505,12 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int T, i
     perm_scan_kernel<<<1, kPermThreads, l2, st>>>(scratch, groups, E, S, counts, slot_offsets, miss_count, err);
     perm_scatter_kernel<<<groups, kPermThreads, l3, st>>>(topk_idx, topk_w, R, k, E, slot_map, S, scratch, perm,
                                                           inv_perm, miss_token, miss_expert, miss_weight);
+    return hipGetLastError();
+  }
+  if (R <= kSmallPermRows) {
+    permute_small_kernel<<<1, kPermThreads, sizeof(int32_t) * permute_small_lds_words(R), st>>>(
+        topk_idx, topk_w, T, k, E, slot_map, S, counts, slot_offsets, perm, inv_perm, miss_count, miss_token,
+        miss_expert, miss_weight, err);
     return hipGetLastError();
   }
   const size_t lds = permute_lds_bytes(E, S);

@@ -52,9 +52,15 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
   float my_l = 0.0f;
   my_e = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    // the lane's best key by a pairwise tree (log2 VPL dependent steps)
+    uint64_t b[VPL];
 #pragma unroll
-    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
+    for (int i = 0; i < VPL; ++i) b[i] = key[i];
+#pragma unroll
+    for (int w = 1; w < VPL; w *= 2)
+#pragma unroll
+      for (int i = 0; i + w < VPL; i += 2 * w) b[i] = b[i + w] > b[i] ? b[i + w] : b[i];
+    const uint64_t best = b[0];
     // the largest logit over the wave (high words); its lane, or among equal logits the smallest id
     const uint32_t bh = uint32_t(best >> 32);
     const uint32_t h = wave_max_u32(bh);
@@ -66,15 +72,13 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
       e = int(~wave_max_u32(bh == h ? uint32_t(best) : 0u));
     }
     const float l = __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h);
-    if ((e & 63) == lane) {
+    // the winner's key leaves the race (selects, no branch)
+    const bool mine = (e & 63) == lane;
+    const int col = e >> 6;
 #pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (i == (e >> 6)) key[i] = 0ull;
-    }
-    if (lane == j) {
-      my_l = l;
-      my_e = e;
-    }
+    for (int i = 0; i < VPL; ++i) key[i] = (mine && i == col) ? 0ull : key[i];
+    my_l = lane == j ? l : my_l;
+    my_e = lane == j ? e : my_e;
   }
   // scores of the k chosen (lane j holds the j-th), gates renormalised in ascending j
   const float my_s = (score == 0) ? expf(my_l - mx) / z : 1.0f / (1.0f + expf(-my_l));

@@ -28,6 +28,9 @@ SMALL = {
     # the matrix-core path with FP8 / MXFP4 weights (K multiples of 128): several M tiles per slot
     "fp8_gemm_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=4, I=256, k=2),
     "mxfp4_gemm_groups": gen.config("compact_mxfp4", T=300, H=512, E=12, I=256, k=4, resident=5),
+    # fused routing + permutation with the small-batch ranking: an odd row count (77, over one
+    # wave of rows) with compact misses
+    "mxfp4_compact_r77": gen.config("compact_mxfp4", T=11, H=256, E=40, I=128, k=7, resident=11),
     # more than 2048 rows: the permutation runs as several work-groups (ragged last group), with
     # compact misses
     "mxfp4_multigroup_perm": gen.config("compact_mxfp4", T=700, H=256, E=48, I=128, k=5, resident=17),

@@ -8,38 +8,45 @@ namespace moe {
 
 // ---------------------------------------------------------------------------------------------
 // logits[t, e] = sum_h x[t,h] W_r[e,h] (+ bias[e])
-// One work-group per expert row: thread j owns the row's 16-byte chunks j, j+256, ... (NCH of
-// them, H <= 1024*NCH), loaded once, all in flight together; the activations of kRouterTok tokens
-// are loaded likewise before any arithmetic.  Partial sums are reduced with DPP inside each wave
-// and across the four waves through LDS.
+// A work-group computes kRouterEpw expert rows: thread j owns the rows' 16-byte chunks j, j+256,
+// ... (NCH per row, H <= 1024*NCH), all loaded before any arithmetic; the activations of TOK
+// tokens (TOK >= T rounded up to 1, 2, 4 or 8; larger batches loop over groups of 8) are loaded
+// once per work-group and used for every row it owns, so the activation bytes moved from L2 are
+// shared by kRouterEpw rows.  Partial sums are reduced with DPP inside each wave and across the
+// four waves through LDS.
 // ---------------------------------------------------------------------------------------------
 constexpr int kRouterThreads = 256;
-constexpr int kRouterTok = 8;
+constexpr int kRouterEpw = 2;
 
-template <int XDT, int NCH>
+template <int XDT, int NCH, int TOK>
 __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const void* __restrict__ x_,
                                                                        const float* __restrict__ wr,
                                                                        const float* __restrict__ bias,
                                                                        float* __restrict__ logits,
                                                                        int T, int H, int E) {
-  __shared__ float part[kRouterThreads / 64][kRouterTok];
+  __shared__ float part[kRouterThreads / 64][kRouterEpw][TOK];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int e = blockIdx.x;
-  const float4* wrow = reinterpret_cast<const float4*>(wr + size_t(e) * H);
+  const int e0 = blockIdx.x * kRouterEpw;
   const int nch = H >> 2;
-  const float b = bias ? bias[e] : 0.0f;
-  // chunks past the row re-read its last chunk and are weighted by zero
-  float4 w[NCH];
+  // the bias of the (row, token) pair this thread stores, loaded with the weights
+  const float bv = (bias && tid < kRouterEpw * TOK) ? bias[min(e0 + tid / TOK, E - 1)] : 0.0f;
+  // chunks past the row re-read its last chunk and are weighted by zero; a row past E re-reads
+  // the last row and is not stored
+  float4 w[kRouterEpw][NCH];
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = tid + kRouterThreads * j;
-    w[j] = wrow[min(c, nch - 1)];
-    if (c >= nch) w[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int r = 0; r < kRouterEpw; ++r) {
+    const float4* wrow = reinterpret_cast<const float4*>(wr + size_t(min(e0 + r, E - 1)) * H);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + kRouterThreads * j;
+      w[r][j] = wrow[min(c, nch - 1)];
+      if (c >= nch) w[r][j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
   }
-  for (int t0 = 0; t0 < T; t0 += kRouterTok) {
-    float acc[kRouterTok];
+  for (int t0 = 0; t0 < T; t0 += TOK) {
+    float acc[kRouterEpw][TOK];
 #pragma unroll
-    for (int i = 0; i < kRouterTok; ++i) {
+    for (int i = 0; i < TOK; ++i) {
       const int t = min(t0 + i, T - 1);  // tokens past T repeat the last one (not stored)
       float4 xv[NCH];
 #pragma unroll
@@ -52,27 +59,36 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const voi
           xv[j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
         }
       }
-      float a = 0.0f;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        a = fmaf(w[j].x, xv[j].x, a);
-        a = fmaf(w[j].y, xv[j].y, a);
-        a = fmaf(w[j].z, xv[j].z, a);
-        a = fmaf(w[j].w, xv[j].w, a);
+      for (int r = 0; r < kRouterEpw; ++r) {
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          a = fmaf(w[r][j].x, xv[j].x, a);
+          a = fmaf(w[r][j].y, xv[j].y, a);
+          a = fmaf(w[r][j].z, xv[j].z, a);
+          a = fmaf(w[r][j].w, xv[j].w, a);
+        }
+        acc[r][i] = a;
       }
-      acc[i] = a;
     }
 #pragma unroll
-    for (int i = 0; i < kRouterTok; ++i) {
-      const float s = seg_sum<64>(acc[i]);
-      if (lane == 63) part[wid][i] = s;
-    }
+    for (int r = 0; r < kRouterEpw; ++r)
+#pragma unroll
+      for (int i = 0; i < TOK; ++i) {
+        const float s = seg_sum<64>(acc[r][i]);
+        if (lane == 63) part[wid][r][i] = s;
+      }
     __syncthreads();
-    if (tid < kRouterTok && t0 + tid < T) {
-      float s = 0.0f;
+    if (tid < kRouterEpw * TOK) {
+      const int r = tid / TOK, i = tid - r * TOK;
+      const int e = e0 + r;
+      if (e < E && t0 + i < T) {
+        float s = 0.0f;
 #pragma unroll
-      for (int w2 = 0; w2 < kRouterThreads / 64; ++w2) s += part[w2][tid];
-      logits[size_t(t0 + tid) * E + e] = s + b;
+        for (int w2 = 0; w2 < kRouterThreads / 64; ++w2) s += part[w2][r][i];
+        logits[size_t(t0 + i) * E + e] = s + bv;
+      }
     }
     __syncthreads();
   }
@@ -101,20 +117,29 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 hipError_t launch_router_logits(const void* x, int xdt, const float* wr, const float* bias,
                                 float* logits, int T, int H, int E, hipStream_t st) {
-  dim3 grid(E), block(kRouterThreads);
-  const int nch = (H / 4 + kRouterThreads - 1) / kRouterThreads;  // chunks per thread
-#define MOE_ROUTER_LAUNCH(N)                                                                    \
-  {                                                                                             \
-    if (xdt == DT_F32)                                                                          \
-      router_logits_kernel<DT_F32, N><<<grid, block, 0, st>>>(x, wr, bias, logits, T, H, E);    \
-    else                                                                                        \
-      router_logits_kernel<DT_BF16, N><<<grid, block, 0, st>>>(x, wr, bias, logits, T, H, E);   \
+  dim3 grid((E + kRouterEpw - 1) / kRouterEpw), block(kRouterThreads);
+  const int nch = (H / 4 + kRouterThreads - 1) / kRouterThreads;  // chunks per thread and row
+  const int tok = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+#define MOE_ROUTER_LAUNCH_T(N, TK)                                                                  \
+  {                                                                                                 \
+    if (xdt == DT_F32)                                                                              \
+      router_logits_kernel<DT_F32, N, TK><<<grid, block, 0, st>>>(x, wr, bias, logits, T, H, E);    \
+    else                                                                                            \
+      router_logits_kernel<DT_BF16, N, TK><<<grid, block, 0, st>>>(x, wr, bias, logits, T, H, E);   \
+  }
+#define MOE_ROUTER_LAUNCH(N)                         \
+  {                                                  \
+    if (tok == 1) MOE_ROUTER_LAUNCH_T(N, 1)          \
+    else if (tok == 2) MOE_ROUTER_LAUNCH_T(N, 2)     \
+    else if (tok == 4) MOE_ROUTER_LAUNCH_T(N, 4)     \
+    else MOE_ROUTER_LAUNCH_T(N, 8)                   \
   }
   if (nch <= 1) MOE_ROUTER_LAUNCH(1)
   else if (nch <= 2) MOE_ROUTER_LAUNCH(2)
   else if (nch <= 4) MOE_ROUTER_LAUNCH(4)
   else MOE_ROUTER_LAUNCH(8)
 #undef MOE_ROUTER_LAUNCH
+#undef MOE_ROUTER_LAUNCH_T
   return hipGetLastError();
 }
 

@@ -34,6 +34,10 @@ SMALL = {
     # more than 2048 rows: the permutation runs as several work-groups (ragged last group), with
     # compact misses
     "mxfp4_multigroup_perm": gen.config("compact_mxfp4", T=700, H=256, E=48, I=128, k=5, resident=17),
+    # router logits for 3 and 1 tokens with an odd expert count (the last work-group owns one
+    # expert row); router bias on the first
+    "bf16_router_t3": gen.config("decode_bf16", T=3, H=256, E=13, I=128, k=2),
+    "bf16_router_t1": gen.config("decode_bf16", T=1, H=320, E=7, I=64, k=3),
     # down-projection rows of exactly 64 16-byte chunks (16 lanes per row, two rows per step)
     "fp8_down64": gen.config("decode_fp8", T=29, H=256, E=20, I=1024, k=3),
     "bf16_down64": gen.config("decode_bf16", T=6, H=256, E=12, I=512, k=2),
@@ -62,7 +66,7 @@ def small_case(request):
     _gpu()
     from gpu_cases import GpuCase, run_oracle
     cfg = SMALL[request.param]
-    inp = gen.make_inputs(cfg, bias=(request.param == "bf16_ragged"))
+    inp = gen.make_inputs(cfg, bias=request.param in ("bf16_ragged", "bf16_router_t3"))
     return request.param, inp, GpuCase(inp), run_oracle(inp)
 
 

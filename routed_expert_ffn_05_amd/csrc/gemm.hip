@@ -8,11 +8,13 @@
 // runs only ceil(rows/32) row blocks, so a slot of n rows costs that much matrix work while its
 // weights are streamed once per 128-row M tile.  The wide N tile halves how often each activation
 // row is moved from L2 into LDS (the on-chip traffic that bounds these GEMMs).
-// Staging.  Operand tiles of each K step (BK = 64) move from HBM to LDS by direct LDS loads
-// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane) with no register
-// staging; one explicit vmcnt wait and one barrier per step, the loads of a step spread over its
-// MFMA sub-steps.  One work-group per CU owns most of the LDS: a stage holds the A rows the tile
-// uses plus the B tile, and tiles with fewer row blocks keep more K steps in flight (3 to 8).
+// Staging.  Operand tiles of each K step (BK = 128 for FP8 and MXFP4 weights, 64 for bf16: a
+// weight row segment per step is a whole 128-byte line where LDS allows) move from HBM to LDS by
+// direct LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane)
+// with no register staging; one explicit vmcnt wait and one barrier per step, the loads of a step
+// spread over its MFMA sub-steps.  One work-group per CU owns most of the LDS: a stage holds the
+// A rows the tile uses plus the B tile, and tiles with fewer row blocks keep more K steps in
+// flight (2 for a full FP8 tile, up to 8).
 // Within a row, the 16-byte granule g of row r is stored at slot g ^ f(r) (f spreads consecutive
 // rows over distinct bank groups for the MFMA fragment reads).  Weights stay in their stored
 // format in LDS and are decoded when a B fragment is read: e4m3fn -> bf16 is exact; e2m1 times a
@@ -439,8 +441,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 // Mode B: block-scaled low-precision matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4).  A = E4M3
 // activation codes with one E8M0 scale per row and 32 K (quantised beforehand), B = the stored
 // weights: E4M3 (scale operand 1.0, the 128x128 block scale folded in per K block as in mode A)
-// or E2M1 with its own E8M0 scales.  One MFMA covers a 64-wide K step; operand lanes: lane (r, h)
-// holds 8-bit K granules h and 2+h (16 elements each) of the step, or 4-bit K [32h, 32h+32);
+// or E2M1 with its own E8M0 scales.  One MFMA covers 64 K (a 128-wide K step of the kernel takes
+// two); operand lanes: lane (r, h) holds 8-bit K granules h and 2+h (16 elements each) of its 64,
+// or 4-bit K [32h, 32h+32);
 // lane r+32b supplies the scale of K block b of row (column) r.
 // GATEUP = true:  A = quantised x rows (through perm), out a (fp32, quantised again before down)
 // GATEUP = false: A = quantised a rows (positions),    out y (fp32)

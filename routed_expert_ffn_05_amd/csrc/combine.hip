@@ -17,7 +17,9 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
                                                                void* __restrict__ out) {
   const int t = blockIdx.x;
   const int h = (blockIdx.y * kCombThreads + threadIdx.x) * 4;
-  if (h >= H) return;
+  // lanes past H stay active: the positions and gates are read across the wave (readlane), so every
+  // lane loads its own; only their row loads and stores are skipped
+  const bool live = h < H;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   // the token's positions and gates, one per lane (k <= 64), in one load each; then groups of kJ
   // choices: every row load of a group in flight together, the sums in ascending j
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
     for (int u = 0; u < kJ; ++u) {
       p[u] = __builtin_amdgcn_readlane(pv, j0 + u);
       g[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j0 + u));
-      if (j0 + u >= k || p[u] >= cap) p[u] = -1;
+      if (j0 + u >= k || p[u] >= cap || !live) p[u] = -1;
     }
     float4 v[kJ];
 #pragma unroll
@@ -50,6 +52,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
       }
     }
   }
+  if (!live) return;
   if constexpr (ODT == DT_F32) {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + size_t(t) * H + h) = acc;
   } else {

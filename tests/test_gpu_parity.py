@@ -38,6 +38,12 @@ SMALL = {
     # expert row); router bias on the first
     "bf16_router_t3": gen.config("decode_bf16", T=3, H=256, E=13, I=128, k=2),
     "bf16_router_t1": gen.config("decode_bf16", T=1, H=320, E=7, I=64, k=3),
+    # the largest expert count and top-k the ABI takes (E = 1024: 16 values per lane in the top-k;
+    # k = 64): 128 rows (the last size ranked by direct counts), 192 rows (counter passes in the
+    # fused kernel), and a compact map of 700 resident experts out of 1024 with misses
+    "max_e_k_r128": gen.config("decode_bf16", T=2, H=128, E=1024, I=64, k=64),
+    "max_e_k_r192": gen.config("decode_bf16", T=3, H=128, E=1024, I=64, k=64),
+    "max_e_k_compact": gen.config("compact_mxfp4", T=2, H=128, E=1024, I=128, k=64, resident=700),
     # down-projection rows of exactly 64 16-byte chunks (16 lanes per row, two rows per step)
     "fp8_down64": gen.config("decode_fp8", T=29, H=256, E=20, I=1024, k=3),
     "bf16_down64": gen.config("decode_bf16", T=6, H=256, E=12, I=512, k=2),

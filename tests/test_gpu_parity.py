@@ -44,6 +44,9 @@ SMALL = {
     "max_e_k_r128": gen.config("decode_bf16", T=2, H=128, E=1024, I=64, k=64),
     "max_e_k_r192": gen.config("decode_bf16", T=3, H=128, E=1024, I=64, k=64),
     "max_e_k_compact": gen.config("compact_mxfp4", T=2, H=128, E=1024, I=128, k=64, resident=700),
+    # degenerate routing: every expert chosen (k = E), and a single expert (E = k = 1)
+    "k_equals_e": gen.config("decode_bf16", T=5, H=256, E=8, I=128, k=8),
+    "single_expert": gen.config("decode_bf16", T=7, H=256, E=1, I=64, k=1),
     # down-projection rows of exactly 64 16-byte chunks (16 lanes per row, two rows per step)
     "fp8_down64": gen.config("decode_fp8", T=29, H=256, E=20, I=1024, k=3),
     "bf16_down64": gen.config("decode_bf16", T=6, H=256, E=12, I=512, k=2),

@@ -104,6 +104,7 @@ typedef struct moe_routing {
  * Exactly one of w_router / logits is non-NULL.
  *   x         device [T, H], x_dtype MOE_F32 or MOE_BF16; unused (may be NULL) with `logits`
  *   w_router  device fp32 [E, H]: logits are computed as x . W_r^T, fp32 accumulation
+ *             (H a multiple of 4, at most 8192; MOE_ERR_UNSUPPORTED otherwise)
  *   logits    device fp32 [T, E]: logits handed in directly
  *   bias      device fp32 [E] or NULL, added to the logits in fp32 before selection
  *   topk_idx  device int32 [T, k] out: expert ids, descending logit, ties to the smaller id

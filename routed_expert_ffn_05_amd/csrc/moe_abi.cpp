@@ -220,7 +220,8 @@ int moe_route(const void* x, int x_dtype, int T, int H, const float* w_router, c
   if (T > 0 && (!topk_idx || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_w is NULL");
   if (w_router) {
     MOE_TRY(check_act_dtype(x_dtype, "x"));
-    if (H < 4 || H % 4) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 4", H);
+    if (H < 4 || H % 4 || H > kMaxDim)
+      return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 4, at most %d", H, kMaxDim);
     if (T > 0 && !x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
     if (!aligned(x, 16) || !aligned(w_router, 16)) return fail(MOE_ERR_INVALID_ARG, "x / w_router must be 16-byte aligned");
     if (!logits_out && ws_bytes < moe_route_workspace_size(T, cfg, 1))
@@ -463,7 +464,8 @@ int moe_route_permute(const void* x, int x_dtype, int T, int H, const float* w_r
     return fail(MOE_ERR_INVALID_ARG, "a slot_map needs miss_count, miss_token, miss_expert and miss_weight");
   if (w_router) {
     MOE_TRY(check_act_dtype(x_dtype, "x"));
-    if (H < 4 || H % 4) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 4", H);
+    if (H < 4 || H % 4 || H > kMaxDim)
+      return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 4, at most %d", H, kMaxDim);
     if (T > 0 && !x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
     if (!aligned(x, 16) || !aligned(w_router, 16)) return fail(MOE_ERR_INVALID_ARG, "x / w_router must be 16-byte aligned");
   }

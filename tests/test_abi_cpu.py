@@ -77,6 +77,11 @@ def test_route_validation(L):
             None, 0, 0)
     _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_route, FAKE + 4, moe.MOE_F32, 4, 64, FAKE, None, None, cfg, FAKE,
             FAKE, None, FAKE, 1 << 20, 0)
+    # the router GEMV covers H up to 8192 (8 chunks of 4 per thread, 256 threads)
+    _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_route, FAKE, moe.MOE_F32, 4, 8196, FAKE, None, None, cfg, FAKE,
+            FAKE, None, FAKE, 1 << 20, 0)
+    _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_route_permute, FAKE, moe.MOE_F32, 4, 8196, FAKE, None, None, cfg,
+            None, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, 1 << 20, 0)
     msg = _expect(moe.MOE_ERR_WORKSPACE, moe.moe_route, FAKE, moe.MOE_F32, 4, 64, FAKE, None, None, cfg, FAKE,
                   FAKE, None, FAKE, 16, 0)
     assert "need" in msg

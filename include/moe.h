@@ -193,6 +193,25 @@ int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_
                 int H, void* out, int out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_combine_tiers -- moe_combine over two tiers of computed rows: the consumer of the compact
+ * miss list.  The pages compute the rows routed to absent experts on another tier and add them
+ * to the compact output, which then equals the all-resident output (vLLM-Moet README, the
+ * compact MoE calls and CPU-computed rows; MoET hybrid table, row "identity").  Here the other
+ * tier is a second weight pool with its own slot map: run moe_permute with a map that sends
+ * exactly the experts absent from tier a to pool slots (and the others to -1), and
+ * moe_expert_ffn on that pool, which gives y_b and inv_b.
+ *   y_a, inv_a   tier a rows: fp32 [*, H] and int32 [T*k] positions (-1: not in tier a)
+ *   y_b, inv_b   tier b rows, likewise; both NULL = moe_combine
+ *   out[t] = sum over j ascending of topk_w[t,j] * (y_a[inv_a[r]] if inv_a[r] >= 0, else
+ *            y_b[inv_b[r]] if inv_b[r] >= 0, else nothing), r = t*k + j, fp32, one rounding.
+ * Positions at or past T*k count as absent.  Summed in the same order as moe_combine over one
+ * pool holding both tiers' experts, so with the same FFN path the output equals that of the
+ * one-pool layer bit for bit.  Errors as moe_combine; y_b and inv_b must be given together.
+ * ------------------------------------------------------------------------------------------ */
+int moe_combine_tiers(const float* y_a, const int32_t* inv_a, const float* y_b, const int32_t* inv_b,
+                      const float* topk_w, int T, int k, int H, void* out, int out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_layer -- route, permute, expert FFN and combine in one call, one workspace, no host
  * synchronisation.
  *   x, x_dtype, T, w_router / logits, bias, cfg   as moe_route (H = w->H)

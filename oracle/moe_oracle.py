@@ -286,6 +286,25 @@ def combine(y_perm: np.ndarray, inv_perm: np.ndarray, topk_w: np.ndarray, T: int
     return out
 
 
+def combine_tiers(y_a: np.ndarray, inv_a: np.ndarray, y_b: np.ndarray, inv_b: np.ndarray,
+                  topk_w: np.ndarray, T: int, k: int, H: int) -> np.ndarray:
+    """The combine over two tiers of computed rows (the compact call's resident slots and the
+    other tier that computes the rows routed to absent experts -- README, MoET hybrid table,
+    row "identity"): row (t, j) takes its output from tier a where it has a position there,
+    else from tier b, else adds nothing; j ascending."""
+    out = np.zeros((T, H))
+    w = np.asarray(topk_w, np.float64).reshape(T, k)
+    ia = np.asarray(inv_a).reshape(T, k)
+    ib = np.asarray(inv_b).reshape(T, k)
+    for t in range(T):
+        for j in range(k):
+            if ia[t, j] >= 0:
+                out[t] += w[t, j] * y_a[ia[t, j]]
+            elif ib[t, j] >= 0:
+                out[t] += w[t, j] * y_b[ib[t, j]]
+    return out
+
+
 # ----------------------------------------------------------------------------------------------
 # mode-B activation quantisation mirror (a defined step of the low-precision MFMA path)
 # ----------------------------------------------------------------------------------------------

@@ -59,6 +59,7 @@ _SIGS = {
     "moe_expert_gate_up": (_I, [_W, _P, _I, _I, _I, _P, _P, _I, _I, _P, _Z, _P]),
     "moe_expert_down": (_I, [_W, _I, _I, _P, _I, _I, _P, _P, _Z, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_combine_tiers": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_layer_workspace_size": (_Z, [_I, _R, _W, _I, _I, _I]),
     "moe_layer": (_I, [_P, _I, _I, _P, _P, _P, _R, _P, _W, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                        _P, _Z, _P]),
@@ -206,6 +207,11 @@ def moe_quantize_mx_e4m3(x, x_dtype, rows, K, codes=None, scales=None, deq=None,
 def moe_combine(y_perm, inv_perm, topk_w, T, k, H, out, out_dtype, stream=None):
     _check(lib().moe_combine(_ptr(y_perm), _ptr(inv_perm), _ptr(topk_w), T, k, H, _ptr(out), out_dtype,
                              _stream(stream)), "moe_combine")
+
+
+def moe_combine_tiers(y_a, inv_a, y_b, inv_b, topk_w, T, k, H, out, out_dtype, stream=None):
+    _check(lib().moe_combine_tiers(_ptr(y_a), _ptr(inv_a), _ptr(y_b), _ptr(inv_b), _ptr(topk_w), T, k, H,
+                                   _ptr(out), out_dtype, _stream(stream)), "moe_combine_tiers")
 
 
 def moe_layer_workspace_size(T, cfg, w, path, mode, with_router_weights) -> int:

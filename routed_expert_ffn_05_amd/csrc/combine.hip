@@ -1,7 +1,11 @@
-// Weighted combine back to token order: out[t] = sum_j w[t,j] * y_perm[inv_perm[t*k+j]] over the
-// resident rows, j ascending, fp32, rounded once to the output format.  Each thread owns four
-// consecutive hidden columns of one token (16-byte loads of the fp32 rows), so the sum order is
-// fixed and the result deterministic.
+// Weighted combine back to token order: out[t] = sum_j w[t,j] * y[row (t,j)] over the computed
+// rows, j ascending, fp32, rounded once to the output format.  A row's output comes from tier a
+// (y_a[inv_a[t*k+j]]) when it has a position there, else from tier b (y_b[inv_b[t*k+j]]) when one
+// is given and the row has a position in it, else the row adds nothing.  With tier b a second
+// weight pool holding the experts tier a lacks, the result is the one-pool layer on the union
+// of the pools, summed in the same order.  Each thread owns four consecutive hidden columns of
+// one token (16-byte loads of the fp32 rows), so the sum order is fixed and the result
+// deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,6 +16,8 @@ constexpr int kCombThreads = 256;
 template <int ODT>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __restrict__ y,
                                                                const int32_t* __restrict__ inv,
+                                                               const float* __restrict__ y_b,
+                                                               const int32_t* __restrict__ inv_b,
                                                                const float* __restrict__ w, int T,
                                                                int k, int H, int cap,
                                                                void* __restrict__ out) {
@@ -25,26 +31,32 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
   // choices: every row load of a group in flight together, the sums in ascending j
   const int lane = threadIdx.x & 63;
   const int pv = lane < k ? inv[size_t(t) * k + lane] : -1;
+  const int qv = (inv_b && lane < k) ? inv_b[size_t(t) * k + lane] : -1;
   const float gv = lane < k ? w[size_t(t) * k + lane] : 0.0f;
   constexpr int kJ = 8;
   for (int j0 = 0; j0 < k; j0 += kJ) {
-    int p[kJ];
+    const float* src[kJ];  // the row's output in tier a or b, or none
     float g[kJ];
 #pragma unroll
     for (int u = 0; u < kJ; ++u) {
-      p[u] = __builtin_amdgcn_readlane(pv, j0 + u);
+      const int p = __builtin_amdgcn_readlane(pv, j0 + u);
+      const int q = __builtin_amdgcn_readlane(qv, j0 + u);
       g[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j0 + u));
-      if (j0 + u >= k || p[u] >= cap || !live) p[u] = -1;
+      src[u] = nullptr;
+      if (live && j0 + u < k) {
+        if (p >= 0 && p < cap) src[u] = y + size_t(p) * H + h;
+        else if (q >= 0 && q < cap) src[u] = y_b + size_t(q) * H + h;
+      }
     }
     float4 v[kJ];
 #pragma unroll
     for (int u = 0; u < kJ; ++u) {
       v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (p[u] >= 0) v[u] = *reinterpret_cast<const float4*>(y + size_t(p[u]) * H + h);
+      if (src[u]) v[u] = *reinterpret_cast<const float4*>(src[u]);
     }
 #pragma unroll
     for (int u = 0; u < kJ; ++u) {
-      if (p[u] >= 0) {
+      if (src[u]) {
         acc.x = fmaf(g[u], v[u].x, acc.x);
         acc.y = fmaf(g[u], v[u].y, acc.y);
         acc.z = fmaf(g[u], v[u].z, acc.z);
@@ -63,14 +75,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
   }
 }
 
-hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int T, int k, int H,
-                          void* out, int odt, hipStream_t st) {
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* y_b, const int32_t* inv_b,
+                          const float* w, int T, int k, int H, void* out, int odt, hipStream_t st) {
   dim3 grid(T, (H / 4 + kCombThreads - 1) / kCombThreads), block(kCombThreads);
   const int cap = T * k;
   if (odt == DT_F32)
-    combine_kernel<DT_F32><<<grid, block, 0, st>>>(y, inv, w, T, k, H, cap, out);
+    combine_kernel<DT_F32><<<grid, block, 0, st>>>(y, inv, y_b, inv_b, w, T, k, H, cap, out);
   else
-    combine_kernel<DT_BF16><<<grid, block, 0, st>>>(y, inv, w, T, k, H, cap, out);
+    combine_kernel<DT_BF16><<<grid, block, 0, st>>>(y, inv, y_b, inv_b, w, T, k, H, cap, out);
   return hipGetLastError();
 }
 

@@ -84,7 +84,7 @@ hipError_t launch_gemm_down_q(const GemmArgs& g, hipStream_t st);
 hipError_t launch_act_quant(const void* in, int in_dt, int rows, int K, const int32_t* nrows, uint8_t* codes,
                             uint8_t* scales, void* deq, int deq_dt, hipStream_t st);
 
-hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int T, int k, int H,
-                          void* out, int odt, hipStream_t st);
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* y_b, const int32_t* inv_b,
+                          const float* w, int T, int k, int H, void* out, int odt, hipStream_t st);
 
 }  // namespace moe

@@ -425,14 +425,21 @@ int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int 
 // ---------------------------------------------------------------------------------------------
 int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int T, int k,
                 int H, void* out, int out_dtype, void* stream) {
+  return moe_combine_tiers(y_perm, inv_perm, nullptr, nullptr, topk_w, T, k, H, out, out_dtype, stream);
+}
+
+int moe_combine_tiers(const float* y_a, const int32_t* inv_a, const float* y_b, const int32_t* inv_b,
+                      const float* topk_w, int T, int k, int H, void* out, int out_dtype, void* stream) {
   if (k < 1 || k > kMaxK) return fail(MOE_ERR_INVALID_ARG, "k = %d out of range", k);
   MOE_TRY(check_T(T, k));
   if (H < 4 || H % 4) return fail(MOE_ERR_UNSUPPORTED, "H = %d must be a positive multiple of 4", H);
   MOE_TRY(check_act_dtype(out_dtype, "out"));
-  if (T > 0 && (!y_perm || !inv_perm || !topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "a NULL pointer");
-  if (!aligned(y_perm, 16) || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "y_perm / out must be 16-byte aligned");
+  if ((y_b == nullptr) != (inv_b == nullptr)) return fail(MOE_ERR_INVALID_ARG, "give both y_b and inv_b or neither");
+  if (T > 0 && (!y_a || !inv_a || !topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "a NULL pointer");
+  if (!aligned(y_a, 16) || !aligned(y_b, 16) || !aligned(out, 16))
+    return fail(MOE_ERR_INVALID_ARG, "y_a / y_b / out must be 16-byte aligned");
   if (T == 0) return MOE_OK;
-  hipError_t e = moe::launch_combine(y_perm, inv_perm, topk_w, T, k, H, out, out_dtype, as_stream(stream));
+  hipError_t e = moe::launch_combine(y_a, inv_a, y_b, inv_b, topk_w, T, k, H, out, out_dtype, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "combine");
   return MOE_OK;
 }

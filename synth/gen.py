@@ -248,6 +248,19 @@ def make_slot_map(cfg: Config):
     return sm, pi[: cfg.resident].copy()
 
 
+def make_pool_map(cfg: Config):
+    """(pool_map [E] int32, pool_expert [P] int32): the second weight pool of a compact config,
+    holding exactly the experts without a resident slot (in the order of the same seeded
+    permutation), pool_map[e] = its pool slot, -1 for the resident experts."""
+    if cfg.resident is None:
+        raise ValueError("a pool map needs a compact config")
+    pi = _rng(cfg, _SLOTS).permutation(cfg.E).astype(np.int32)
+    absent = pi[cfg.resident:]
+    pm = np.full(cfg.E, -1, np.int32)
+    pm[absent] = np.arange(absent.size, dtype=np.int32)
+    return pm, absent.copy()
+
+
 @dataclasses.dataclass
 class LayerInputs:
     cfg: Config

@@ -182,6 +182,22 @@ class GpuCase:
         return (D.bf16_bits_to_float(o) if self.odt == moe.MOE_BF16 else o).astype(np.float64)
 
 
+    def combine_tiers(self, y_a, inv_a, y_b, inv_b, topk_w):
+        torch = self.torch
+        c = self.cfg
+
+        def rows(y):
+            return D.to_device(np.ascontiguousarray(y, np.float32)) if len(y) else \
+                torch.zeros((1, c.H), dtype=torch.float32, device="cuda")
+        out = torch.empty((c.T, c.H), dtype=torch.int16 if self.odt == moe.MOE_BF16 else torch.float32, device="cuda")
+        moe.moe_combine_tiers(rows(y_a), D.to_device(np.asarray(inv_a, np.int32)), rows(y_b),
+                              D.to_device(np.asarray(inv_b, np.int32)), D.to_device(np.asarray(topk_w, np.float32)),
+                              c.T, c.k, c.H, out, self.odt)
+        torch.cuda.synchronize()
+        o = D.to_host(out)
+        return (D.bf16_bits_to_float(o) if self.odt == moe.MOE_BF16 else o).astype(np.float64)
+
+
 def routing_mismatches(gpu_idx, ref):
     """Tokens whose GPU selection differs from the oracle's; asserts each one is a flagged near-tie."""
     diff = np.nonzero((np.asarray(gpu_idx) != ref["topk_idx"]).any(axis=1))[0]

@@ -150,6 +150,12 @@ def test_combine_and_layer_validation(L):
     _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_combine, FAKE, FAKE, FAKE, 4, 2, 30, FAKE, moe.MOE_F32, 0)
     _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_combine, FAKE, FAKE, FAKE, 4, 2, 64, FAKE, 3, 0)
     _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_combine, FAKE, None, FAKE, 4, 2, 64, FAKE, moe.MOE_F32, 0)
+    # two tiers: y_b and inv_b together, y_b 16-byte aligned
+    ct = moe.moe_combine_tiers
+    _expect(moe.MOE_ERR_INVALID_ARG, ct, FAKE, FAKE, FAKE, None, FAKE, 4, 2, 64, FAKE, moe.MOE_F32, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, ct, FAKE, FAKE, None, FAKE, FAKE, 4, 2, 64, FAKE, moe.MOE_F32, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, ct, FAKE, FAKE, FAKE + 4, FAKE, FAKE, 4, 2, 64, FAKE, moe.MOE_F32, 0)
+    _expect(moe.MOE_ERR_UNSUPPORTED, ct, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 30, FAKE, moe.MOE_F32, 0)
     cfg = moe.routing(16, 2, "sigmoid")
     w = moe.weights("bf16", 16, 256, 128, FAKE, None, FAKE, None)
     big = moe.moe_layer_workspace_size(4, cfg, w, moe.MOE_PATH_AUTO, moe.MOE_MODE_A, 0)

@@ -299,6 +299,33 @@ def test_compact_plus_misses_equals_all_resident():
     assert np.array_equal(compact["counts"], full["counts"])
 
 
+def test_two_tiers_equal_one_pool():
+    # the resident tier plus a second pool holding exactly the absent experts, combined in row
+    # order, is the all-resident layer: the same rows, the same per-row FFN, the same sum order
+    for cfg in (SHRUNK["mxfp4_compact"], SHRUNK["mxfp4_compact"].replace(T=1, k=2)):
+        inp = gen.make_inputs(cfg)
+        a = run_oracle(inp)
+        pm, pool = gen.make_pool_map(cfg)
+        assert np.all((pm >= 0) == (inp.slot_map < 0))
+        pw = gen.stack_weights(cfg, pool)
+        b = O.layer(inp.x, cfg.xdtype, pw, cfg.wdtype, cfg.H, cfg.I, cfg.E, cfg.k, cfg.score,
+                    logits=inp.logits, slot_map=pm, S=pool.size)
+        full = O.layer(inp.x, cfg.xdtype, gen.stack_weights(cfg, range(cfg.E)), cfg.wdtype, cfg.H, cfg.I,
+                       cfg.E, cfg.k, cfg.score, logits=inp.logits)
+        # tier b computes exactly tier a's miss rows, in the same row order
+        rows_b = b["perm"]
+        miss_rows = np.nonzero(a["inv_perm"] < 0)[0]
+        assert np.array_equal(np.sort(rows_b), miss_rows)
+        e_b = a["topk_idx"].reshape(-1)[rows_b]
+        assert np.all(inp.slot_map[e_b] < 0) and np.all(pm[e_b] >= 0)
+        out = O.combine_tiers(a["y_perm"], a["inv_perm"], b["y_perm"], b["inv_perm"], a["topk_w"], cfg.T, cfg.k, cfg.H)
+        assert np.array_equal(out, full["out"])
+        # with no tier b rows it is the compact combine
+        none = np.full(cfg.T * cfg.k, -1)
+        assert np.array_equal(O.combine_tiers(a["y_perm"], a["inv_perm"], b["y_perm"], none, a["topk_w"], cfg.T,
+                                              cfg.k, cfg.H), a["out"])
+
+
 def test_token_permutation_equivariance():
     cfg = SHRUNK["fp8"]
     inp = gen.make_inputs(cfg)

@@ -9,7 +9,10 @@ HBM before the timed region starts.  Batches rotate over ``--rotate`` pre-genera
 (or logit) sets so that consecutive steps route to different experts.  Prints ONE JSON line.
 
 The default workload is the bf16 decode layer: T=4 tokens, hidden 4096, 384 experts, expert
-intermediate 1024, top-8 sigmoid routing with renormalised gates.
+intermediate 1024, top-8 sigmoid routing with renormalised gates.  ``--tiers`` (compact configs)
+adds the second tier to every step: the rows routed to absent experts are permuted over a pool
+holding those experts, computed there, and combined with the resident rows (moe_combine_tiers),
+so the step produces the full layer output.
 
 The ``roofline`` object describes the dominant kernel (the expert gate/up projection, 2/3 of the
 layer's bytes): algorithmic bytes per launch over its average duration, measured with HIP events
@@ -154,6 +157,52 @@ def recorded_traffic(workload_key):
 # the benchmark
 # ---------------------------------------------------------------------------------------------
 
+def graph_timing(args, step, w, stream, out, T, S, H, I, cfg, D, torch, log):
+    """Time the layer as replays of one HIP graph of L consecutive layers (launch-bound small
+    batches): layer l runs on its own device copy of the weights (same bytes, other addresses, so
+    no layer finds another's weights in a cache) and on rotation l.  The replayed output of the last
+    layer is checked against the eager step, before and after the timed replays."""
+    L = args.graph_layers
+    wbytes = w.nbytes_per_slot * S
+    ncopy = max(1, min(L, int(64e9 // max(wbytes, 1))))
+    copies = [w] + [D.DeviceWeights(w.wdtype, S, H, I, *[t.clone() if t is not None else None
+                                                         for t in (w.w_gu, w.s_gu, w.w_d, w.s_d)])
+                    for _ in range(ncopy - 1)]
+    descs = [c.desc for c in copies]
+    step(L - 1, dsc=descs[(L - 1) % ncopy])
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap):
+        for l in range(L):
+            step(l, dsc=descs[l % ncopy], sp=cap.cuda_stream)
+    torch.cuda.synchronize()
+
+    def check(when):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise SystemExit(f"bench: graph replay ({when}) differs from the eager step")
+    check("first")
+    n = max(2, args.steps // L)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    check("after timing")
+    us = ms * 1e3 / L
+    log(f"graph: {n} replays of {L} layers ({ncopy} weight copies): {ms * 1e3:.1f} us per replay, "
+        f"{us:.2f} us per layer, {T / (us * 1e-6):.0f} tokens/s")
+    del g
+    return dict(layers=L, weight_copies=ncopy, us_per_layer=us, tokens_per_s=T / (us * 1e-6))
+
+
 def run(args):
     import numpy as np
     import torch
@@ -178,6 +227,19 @@ def run(args):
     w = D.upload_weights(cfg.wdtype, H, I, host_w)
     if not args.cpu_baseline:
         host_w = None
+    tiers = bool(args.tiers)
+    if tiers and args.graph_layers:
+        raise SystemExit("--tiers and --graph-layers are not combined")
+    if tiers:
+        # the second tier: a pool holding every expert without a resident slot, computing the
+        # compact call's miss rows; both tiers are combined in row order
+        if slot_map is None:
+            raise SystemExit("--tiers needs a compact config (a resident subset of the experts)")
+        pool_map, pool_exp = gen.make_pool_map(cfg)
+        P = int(pool_exp.size)
+        t0 = time.time()
+        w_pool = D.upload_weights(cfg.wdtype, H, I, gen.stack_weights(cfg, pool_exp))
+        log(f"generated the pool tier ({P} experts) in {time.time() - t0:.1f}s")
     rot = []
     for r in range(args.rotate):
         rc = cfg.replace(seed=cfg.seed * 1000 + 17 + r) if r else cfg
@@ -213,21 +275,44 @@ def run(args):
     fbytes = moe.moe_expert_ffn_workspace_size(desc, T, k, path, mode)
     fws = D.workspace(fbytes)
     compact = d_sm is not None
+    if tiers:
+        d_pm = D.to_device(pool_map)
+        desc_b = w_pool.desc
+        counts_b = torch.empty(E, dtype=torch.int32, device=dev)
+        off_b = torch.empty(P + 1, dtype=torch.int32, device=dev)
+        perm_b = torch.empty(R, dtype=torch.int32, device=dev)
+        inv_b = torch.empty(R, dtype=torch.int32, device=dev)
+        mc_b = torch.zeros(1, dtype=torch.int32, device=dev)
+        mt_b = torch.empty(R, dtype=torch.int32, device=dev)
+        me_b = torch.empty(R, dtype=torch.int32, device=dev)
+        mw_b = torch.empty(R, dtype=torch.float32, device=dev)
+        y_b = torch.empty((R, H), dtype=torch.float32, device=dev)
+        pb_bytes = moe.moe_permute_workspace_size(T, rcfg, P)
+        pws_b = D.workspace(pb_bytes)
+        fb_bytes = moe.moe_expert_ffn_workspace_size(desc_b, T, k, path, mode)
+        fws_b = D.workspace(fb_bytes)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    def step(i, ev=None):
+    def step(i, ev=None, dsc=None, sp=sp):
         r = i % len(rot)
+        dsc = desc if dsc is None else dsc
         moe.moe_route_permute(d_x[r], xdt, T, H, d_wr, d_lg[r], None, rcfg, d_sm, S, topk_idx, topk_w, counts,
                               off, perm, inv, mc if compact else None, mt if compact else None,
                               me if compact else None, mw if compact else None, pws, rp_bytes, sp)
         if ev is not None:
             ev[0].record(stream)
-        moe.moe_expert_gate_up(desc, d_x[r], xdt, T, k, perm, off, path, mode, fws, fbytes, sp)
+        moe.moe_expert_gate_up(dsc, d_x[r], xdt, T, k, perm, off, path, mode, fws, fbytes, sp)
         if ev is not None:
             ev[1].record(stream)
-        moe.moe_expert_down(desc, T, k, off, path, mode, y, fws, fbytes, sp)
-        moe.moe_combine(y, inv, topk_w, T, k, H, out, odt, sp)
+        moe.moe_expert_down(dsc, T, k, off, path, mode, y, fws, fbytes, sp)
+        if tiers:
+            moe.moe_permute(topk_idx, topk_w, T, rcfg, d_pm, P, counts_b, off_b, perm_b, inv_b, mc_b, mt_b, me_b,
+                            mw_b, pws_b, pb_bytes, sp)
+            moe.moe_expert_ffn(desc_b, d_x[r], xdt, T, k, perm_b, off_b, path, mode, y_b, fws_b, fb_bytes, sp)
+            moe.moe_combine_tiers(y, inv, y_b, inv_b, topk_w, T, k, H, out, odt, sp)
+        else:
+            moe.moe_combine(y, inv, topk_w, T, k, H, out, odt, sp)
 
     # per-rotation routing statistics (outside the timed region)
     per_rot = []
@@ -239,10 +324,12 @@ def run(args):
             res = slot_map >= 0
             touched = int(((cnt > 0) & res).sum())
             n_res = int(cnt[res].sum())
+            touched_b = int(((cnt > 0) & ~res).sum()) if tiers else 0
         else:
             touched = int((cnt > 0).sum())
             n_res = int(cnt.sum())
-        per_rot.append((touched, n_res))
+            touched_b = 0
+        per_rot.append((touched, n_res, touched_b))
     slot_bytes_gu = (w.w_gu.numel() * w.w_gu.element_size() + (0 if w.s_gu is None else w.s_gu.numel() * w.s_gu.element_size())) // S
     slot_bytes_d = (w.w_d.numel() * w.w_d.element_size() + (0 if w.s_d is None else w.s_d.numel() * w.s_d.element_size())) // S
     xb = 2 if cfg.xdtype == "bf16" else 4
@@ -251,15 +338,15 @@ def run(args):
                                          and I % 64 == 0 and T * k > 4 * S)
 
     def gate_up_bytes(r):
-        touched, n_res = per_rot[r]
+        touched, n_res, _ = per_rot[r]
         return touched * slot_bytes_gu + T * H * xb + n_res * I * (2 if gemm else 4)
 
     def gate_up_flops(r):
         return per_rot[r][1] * 2.0 * H * 2 * I
 
     def layer_bytes(r):
-        touched, n_res = per_rot[r]
-        b = touched * (slot_bytes_gu + slot_bytes_d) + T * H * xb + T * H * (2 if odt == moe.MOE_BF16 else 4)
+        touched, n_res, touched_b = per_rot[r]
+        b = (touched + touched_b) * (slot_bytes_gu + slot_bytes_d) + T * H * xb + T * H * (2 if odt == moe.MOE_BF16 else 4)
         b += (E * H * 4) if d_wr is not None else T * E * 4
         return b
 
@@ -289,15 +376,23 @@ def run(args):
         f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s; "
         f"path {'gemm' if gemm else 'gemv'}")
 
-    # the staged step is moe_layer's own sequence: check one rotation bit for bit
-    lay = D.Layer(T=T, H=H, I=I, E=E, k=k, score=cfg.score, renorm=cfg.renorm, xdtype=cfg.xdtype,
+    graph = None
+    if args.graph_layers:
+        graph = graph_timing(args, step, w, stream, out, T, S, H, I, cfg, D, torch, log)
+        tokens_per_s = graph["tokens_per_s"]
+        ms_per_step = graph["us_per_layer"] / 1e3
+
+    # the staged step is moe_layer's own sequence: check one rotation bit for bit (with two tiers
+    # the step goes past moe_layer; their identity with one pool is covered by the GPU tests)
+    lay = None if tiers else D.Layer(T=T, H=H, I=I, E=E, k=k, score=cfg.score, renorm=cfg.renorm, xdtype=cfg.xdtype,
                   out_dtype=cfg.out_dtype, weights=w, w_router=d_wr, slot_map=d_sm, path=path, mode=mode)
-    step(0)
-    lay(d_x[0], d_lg[0])
-    torch.cuda.synchronize()
-    if not torch.equal(lay.out, out):
-        raise SystemExit("bench: staged step and moe_layer disagree")
-    del lay
+    if lay is not None:
+        step(0)
+        lay(d_x[0], d_lg[0])
+        torch.cuda.synchronize()
+        if not torch.equal(lay.out, out):
+            raise SystemExit("bench: staged step and moe_layer disagree")
+        del lay
 
     if args.copy_probe_mib:
         # a plain elementwise kernel that reads nb bytes and writes nb bytes (scales the counters)
@@ -323,7 +418,7 @@ def run(args):
         roofline["mfma_frac_of_bf16_peak"] = round(tflops / MFMA_PEAK_TFLOPS["bf16"], 4)
 
     cpu = None
-    if args.cpu_baseline:
+    if args.cpu_baseline and not tiers:
         cpu = cpu_baseline(cfg, rot, host_w, slot_map, args.cpu_seconds)
 
     rec = {
@@ -341,10 +436,13 @@ def run(args):
                   "mxfp4": "mxfp4 weights, bf16 activations"}[cfg.wdtype],
         "data": "synthetic (seeded; random-init weights of the layer's shape)",
         "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} I={I} k={k} S={S} "
-                               f"{cfg.score}-renorm weights={cfg.wdtype}",
+                               f"{cfg.score}-renorm weights={cfg.wdtype}"
+                               + (f" + pool tier of {P} experts (miss rows computed, both tiers combined)" if tiers else ""),
                    "tokens_per_step": T, "rotations": len(rot), "path": args.path, "mode": args.mode,
                    "layer_algorithmic_GBs": round(layer_gbs, 1),
-                   "touched_slots_per_step": round(float(np.mean([p[0] for p in per_rot])), 2)},
+                   "touched_slots_per_step": round(float(np.mean([p[0] for p in per_rot])), 2),
+                   "timing": (f"HIP graph of {graph['layers']} layers ({graph['weight_copies']} weight copies), "
+                              f"per-layer time of its replays" if graph else "eager launches, HIP events")},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -390,6 +488,10 @@ def main(argv=None):
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--mode", default="A", choices=["A", "B"])
+    ap.add_argument("--graph-layers", type=int, default=0,
+                    help="time the layer as replays of a HIP graph of this many layers (launch-bound batches)")
+    ap.add_argument("--tiers", action="store_true",
+                    help="compact configs: also compute the miss rows from a pool of the absent experts")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0)

@@ -157,6 +157,42 @@ def recorded_traffic(workload_key):
 # the benchmark
 # ---------------------------------------------------------------------------------------------
 
+def plan_hot_set(cfg, seeded_map, moe, D, torch, np, gen, log, batches=8):
+    """Hot-set placement planned on the GPU (moe_accumulate_counts, moe_plan_slots) from the
+    routing of `batches` batches of the same workload that are not timed (other seeds), routed
+    under the seeded map; returns (slot_map, the experts of slots 0..S-1)."""
+    T, H, E, k, S = cfg.T, cfg.H, cfg.E, cfg.k, cfg.S
+    dev = "cuda"
+    R = T * k
+    rcfg = moe.routing(E, k, cfg.score, cfg.renorm)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    off = torch.empty(S + 1, dtype=torch.int32, device=dev)
+    perm, inv, mt, me = (torch.empty(R, dtype=torch.int32, device=dev) for _ in range(4))
+    mw = torch.empty(R, dtype=torch.float32, device=dev)
+    mc = torch.zeros(1, dtype=torch.int32, device=dev)
+    nb = moe.moe_route_permute_workspace_size(T, rcfg, S, False)
+    ws = D.workspace(nb)
+    d_sm = D.to_device(seeded_map)
+    hist = torch.zeros(E, dtype=torch.int64, device=dev)
+    for b in range(batches):
+        lg = D.to_device(gen.make_logits(cfg, batch=1000 + b))
+        moe.moe_route_permute(None, moe.MOE_BF16, T, H, None, lg, None, rcfg, d_sm, S, idx, w, counts, off, perm,
+                              inv, mc, mt, me, mw, ws, nb)
+        moe.moe_accumulate_counts(counts, E, hist)
+    sm = torch.empty(E, dtype=torch.int32, device=dev)
+    moe.moe_plan_slots(hist, E, S, sm)
+    torch.cuda.synchronize()
+    planned = D.to_host(sm)
+    h = D.to_host(hist)
+    experts = np.empty(S, np.int32)
+    experts[planned[planned >= 0]] = np.nonzero(planned >= 0)[0]
+    log(f"hot set planned from {batches} batches: resident-row share {h[planned >= 0].sum() / h.sum():.3f} "
+        f"(seeded map {h[seeded_map >= 0].sum() / h.sum():.3f})")
+    return planned, experts
+
+
 def graph_timing(args, step, w, stream, out, T, S, H, I, cfg, D, torch, log):
     """Time the layer as replays of one HIP graph of L consecutive layers (launch-bound small
     batches): layer l runs on its own device copy of the weights (same bytes, other addresses, so
@@ -218,10 +254,16 @@ def run(args):
     over = {}
     if args.T is not None:
         over["T"] = args.T
+    if args.E is not None:  # e.g. a compute-bound prefill shape: few experts, many rows each
+        over["E"] = args.E
     cfg = gen.config(args.config, **over)
     T, H, I, E, k, S = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.S
     t0 = time.time()
     slot_map, slot_expert = gen.make_slot_map(cfg)
+    if args.plan_slots:
+        if slot_map is None:
+            raise SystemExit("--plan-slots needs a compact config (a resident subset of the experts)")
+        slot_map, slot_expert = plan_hot_set(cfg, slot_map, moe, D, torch, np, gen, log)
     host_w = gen.stack_weights(cfg, slot_expert)
     log(f"generated {cfg.name} weights ({S} slots) in {time.time() - t0:.1f}s")
     w = D.upload_weights(cfg.wdtype, H, I, host_w)
@@ -235,16 +277,22 @@ def run(args):
         # compact call's miss rows; both tiers are combined in row order
         if slot_map is None:
             raise SystemExit("--tiers needs a compact config (a resident subset of the experts)")
-        pool_map, pool_exp = gen.make_pool_map(cfg)
+        pool_exp = np.nonzero(slot_map < 0)[0].astype(np.int32)
+        if not args.plan_slots:
+            _, pool_exp = gen.make_pool_map(cfg)     # the absent experts in the seeded order
+        pool_map = np.full(E, -1, np.int32)
+        pool_map[pool_exp] = np.arange(pool_exp.size, dtype=np.int32)
         P = int(pool_exp.size)
         t0 = time.time()
         w_pool = D.upload_weights(cfg.wdtype, H, I, gen.stack_weights(cfg, pool_exp))
         log(f"generated the pool tier ({P} experts) in {time.time() - t0:.1f}s")
     rot = []
     for r in range(args.rotate):
+        # other activations per rotation; handed-in logits are other batches of the same workload
+        # (same expert popularity, other noise)
         rc = cfg.replace(seed=cfg.seed * 1000 + 17 + r) if r else cfg
         x = gen.make_x(rc)
-        lg = gen.make_logits(rc) if cfg.router != "weights" else None
+        lg = gen.make_logits(cfg, batch=r) if cfg.router != "weights" else None
         rot.append((x, lg))
     d_x = [D.to_device(x) for x, _ in rot]
     d_lg = [D.to_device(lg) if lg is not None else None for _, lg in rot]
@@ -441,6 +489,9 @@ def run(args):
                    "tokens_per_step": T, "rotations": len(rot), "path": args.path, "mode": args.mode,
                    "layer_algorithmic_GBs": round(layer_gbs, 1),
                    "touched_slots_per_step": round(float(np.mean([p[0] for p in per_rot])), 2),
+                   "resident_row_share": round(float(np.mean([p[1] for p in per_rot])) / (T * k), 4),
+                   "slot_map": ("hot set planned on the GPU from 8 untimed batches" if args.plan_slots
+                                else "seeded" if slot_map is not None else "all resident"),
                    "timing": (f"HIP graph of {graph['layers']} layers ({graph['weight_copies']} weight copies), "
                               f"per-layer time of its replays" if graph else "eager launches, HIP events")},
         "roofline": roofline,
@@ -488,6 +539,9 @@ def main(argv=None):
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--mode", default="A", choices=["A", "B"])
+    ap.add_argument("--E", type=int, default=None, help="override the expert count of the config")
+    ap.add_argument("--plan-slots", action="store_true",
+                    help="compact configs: resident slots from the hot-set planner instead of the seeded map")
     ap.add_argument("--graph-layers", type=int, default=0,
                     help="time the layer as replays of a HIP graph of this many layers (launch-bound batches)")
     ap.add_argument("--tiers", action="store_true",

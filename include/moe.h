@@ -248,6 +248,23 @@ int moe_quantize_mx_e4m3(const void* in, int in_dtype, int rows, int K, uint8_t*
                          void* deq, int deq_dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_accumulate_counts / moe_plan_slots -- hot-set placement of the resident slots.  The
+ * recipes wiki (Home page, the expert balance) keeps resident the experts the traffic routes to
+ * most, chosen from routing histograms by a greedy pick of the largest routing share per byte of
+ * weights.  Every expert has the same storage size here, so that share orders as the
+ * accumulated count.
+ *   moe_accumulate_counts: hist[e] += counts[e] for e < E (counts: device int32 [E], e.g. the
+ *       counts output of moe_permute; hist: device int64 [E], 8-byte aligned, zeroed by the
+ *       caller before the first call)
+ *   moe_plan_slots: slot_map[e] (device int32 [E] out) = the rank of e in (hist descending,
+ *       expert id ascending) if that rank is below S, else -1; so slot i holds the i-th hottest
+ *       expert.  1 <= S <= E <= 1024.  Deterministic.
+ * Errors: MOE_ERR_INVALID_ARG for sizes out of range, NULL or misaligned pointers.
+ * ------------------------------------------------------------------------------------------ */
+int moe_accumulate_counts(const int32_t* counts, int E, int64_t* hist, void* stream);
+int moe_plan_slots(const int64_t* hist, int E, int S, int32_t* slot_map, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * helpers
  * ------------------------------------------------------------------------------------------ */
 /* Reads the error word at the start of a moe_permute / moe_route_permute / moe_layer workspace: synchronises

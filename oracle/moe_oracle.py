@@ -305,6 +305,18 @@ def combine_tiers(y_a: np.ndarray, inv_a: np.ndarray, y_b: np.ndarray, inv_b: np
     return out
 
 
+def plan_slots(hist: np.ndarray, S: int) -> np.ndarray:
+    """Hot-set placement (the recipes wiki, Home page, expert balance: the experts with the
+    largest routing share per byte of weights stay resident; equal sizes here, so the largest
+    accumulated counts).  slot_map[e] = rank of e in (count descending, id ascending) when that
+    rank is below S, else -1."""
+    h = np.asarray(hist, np.int64)
+    order = np.lexsort((np.arange(h.size), -h))
+    sm = np.full(h.size, -1, np.int32)
+    sm[order[:S]] = np.arange(S, dtype=np.int32)
+    return sm
+
+
 # ----------------------------------------------------------------------------------------------
 # mode-B activation quantisation mirror (a defined step of the low-precision MFMA path)
 # ----------------------------------------------------------------------------------------------

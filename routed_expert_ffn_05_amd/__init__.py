@@ -60,6 +60,8 @@ _SIGS = {
     "moe_expert_down": (_I, [_W, _I, _I, _P, _I, _I, _P, _P, _Z, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_combine_tiers": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_accumulate_counts": (_I, [_P, _I, _P, _P]),
+    "moe_plan_slots": (_I, [_P, _I, _I, _P, _P]),
     "moe_layer_workspace_size": (_Z, [_I, _R, _W, _I, _I, _I]),
     "moe_layer": (_I, [_P, _I, _I, _P, _P, _P, _R, _P, _W, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                        _P, _Z, _P]),
@@ -212,6 +214,14 @@ def moe_combine(y_perm, inv_perm, topk_w, T, k, H, out, out_dtype, stream=None):
 def moe_combine_tiers(y_a, inv_a, y_b, inv_b, topk_w, T, k, H, out, out_dtype, stream=None):
     _check(lib().moe_combine_tiers(_ptr(y_a), _ptr(inv_a), _ptr(y_b), _ptr(inv_b), _ptr(topk_w), T, k, H,
                                    _ptr(out), out_dtype, _stream(stream)), "moe_combine_tiers")
+
+
+def moe_accumulate_counts(counts, E, hist, stream=None):
+    _check(lib().moe_accumulate_counts(_ptr(counts), E, _ptr(hist), _stream(stream)), "moe_accumulate_counts")
+
+
+def moe_plan_slots(hist, E, S, slot_map, stream=None):
+    _check(lib().moe_plan_slots(_ptr(hist), E, S, _ptr(slot_map), _stream(stream)), "moe_plan_slots")
 
 
 def moe_layer_workspace_size(T, cfg, w, path, mode, with_router_weights) -> int:

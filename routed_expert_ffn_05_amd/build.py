@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmoe_hip.so")
 ARCH = "gfx950"
 
 SOURCES = ["moe_abi.cpp", "router.hip", "permute.hip", "gemv_dispatch.cpp", "gemv_f32.hip", "gemv_bf16.hip",
-           "gemv_fp8.hip", "gemv_mxfp4.hip", "gemm.hip", "combine.hip", "actq.hip"]
+           "gemv_fp8.hip", "gemv_mxfp4.hip", "gemm.hip", "combine.hip", "actq.hip", "plan.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -87,4 +87,8 @@ hipError_t launch_act_quant(const void* in, int in_dt, int rows, int K, const in
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* y_b, const int32_t* inv_b,
                           const float* w, int T, int k, int H, void* out, int odt, hipStream_t st);
 
+// hot-set placement (plan.hip)
+hipError_t launch_accumulate_counts(const int32_t* counts, int E, int64_t* hist, hipStream_t st);
+hipError_t launch_plan_slots(const int64_t* hist, int E, int S, int32_t* slot_map, hipStream_t st);
+
 }  // namespace moe

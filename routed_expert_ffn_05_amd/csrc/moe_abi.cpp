@@ -613,6 +613,25 @@ int moe_quantize_mx_e4m3(const void* in, int in_dtype, int rows, int K, uint8_t*
   return MOE_OK;
 }
 
+int moe_accumulate_counts(const int32_t* counts, int E, int64_t* hist, void* stream) {
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, kMaxE);
+  if (!counts || !hist) return fail(MOE_ERR_INVALID_ARG, "counts / hist is NULL");
+  if (!aligned(hist, 8)) return fail(MOE_ERR_INVALID_ARG, "hist must be 8-byte aligned");
+  hipError_t e = moe::launch_accumulate_counts(counts, E, hist, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "accumulate counts");
+  return MOE_OK;
+}
+
+int moe_plan_slots(const int64_t* hist, int E, int S, int32_t* slot_map, void* stream) {
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, kMaxE);
+  if (S < 1 || S > E) return fail(MOE_ERR_INVALID_ARG, "S = %d must be in [1, E = %d]", S, E);
+  if (!hist || !slot_map) return fail(MOE_ERR_INVALID_ARG, "hist / slot_map is NULL");
+  if (!aligned(hist, 8)) return fail(MOE_ERR_INVALID_ARG, "hist must be 8-byte aligned");
+  hipError_t e = moe::launch_plan_slots(hist, E, S, slot_map, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "plan slots");
+  return MOE_OK;
+}
+
 int moe_check_device_error(const void* ws, void* stream) {
   if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
   uint32_t word = 0;

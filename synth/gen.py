@@ -221,12 +221,14 @@ def zipf_probabilities(cfg: Config) -> np.ndarray:
     return p[rank]
 
 
-def make_logits(cfg: Config) -> np.ndarray:
+def make_logits(cfg: Config, batch: int = 0) -> np.ndarray:
     """[T,E] fp32 router logits for the configs that hand logits in directly.
 
     uniform: U[0,1).  zipf: ln p_e + Gumbel(0,1) noise, so that the top-1 pick of a token is
-    expert e with probability p_e (Gumbel-max) and top-k picks are Gumbel-top-k samples."""
-    g = _rng(cfg, _LOGITS)
+    expert e with probability p_e (Gumbel-max) and top-k picks are Gumbel-top-k samples.
+    ``batch`` selects the noise of another batch of the same workload: the experts' popularity
+    (the Zipf rank permutation) belongs to the config and is shared by every batch."""
+    g = _rng(cfg, _LOGITS) if batch == 0 else _rng(cfg, _LOGITS, batch)
     if cfg.router == "uniform":
         return g.random((cfg.T, cfg.E), dtype=np.float32)
     if cfg.router == "zipf":

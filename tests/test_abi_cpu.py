@@ -176,6 +176,18 @@ def test_combine_and_layer_validation(L):
     _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_layer, *bad)
 
 
+def test_plan_validation(L):
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_accumulate_counts, FAKE, 0, FAKE, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_accumulate_counts, FAKE, 1025, FAKE, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_accumulate_counts, FAKE, 8, FAKE + 4, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_accumulate_counts, None, 8, FAKE, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_plan_slots, FAKE, 8, 9, FAKE, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_plan_slots, FAKE, 8, 0, FAKE, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_plan_slots, FAKE, 2048, 8, FAKE, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_plan_slots, FAKE + 4, 8, 4, FAKE, 0)
+    _expect(moe.MOE_ERR_INVALID_ARG, moe.moe_plan_slots, FAKE, 8, 4, None, 0)
+
+
 def test_last_error_is_per_call(L):
     _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_combine, FAKE, FAKE, FAKE, 4, 2, 30, FAKE, moe.MOE_F32, 0)
     assert "H = 30" in moe.lib().moe_last_error().decode()

@@ -326,6 +326,28 @@ def test_two_tiers_equal_one_pool():
                                               cfg.k, cfg.H), a["out"])
 
 
+def test_plan_slots_brute_force():
+    # the hot set holds the most routed rows of any S experts (brute force over all subsets), its
+    # slots run in rank order, ties go to the smaller expert id
+    from itertools import combinations
+    rng = np.random.default_rng(5)
+    for E, S in ((6, 3), (7, 1), (5, 5), (8, 4)):
+        for trial in range(20):
+            h = rng.integers(0, 4, E).astype(np.int64)   # small values: many ties
+            sm = O.plan_slots(h, S)
+            chosen = np.nonzero(sm >= 0)[0]
+            assert chosen.size == S and sorted(sm[chosen]) == list(range(S))
+            best = max(h[list(c)].sum() for c in combinations(range(E), S))
+            assert h[chosen].sum() == best
+            ranked = chosen[np.argsort(sm[chosen])]
+            for a, b in zip(ranked, ranked[1:]):
+                assert h[a] > h[b] or (h[a] == h[b] and a < b)
+            # every expert left out is colder, or as hot with a larger id, than every chosen one
+            out = np.nonzero(sm < 0)[0]
+            for o in out:
+                assert all(h[c] > h[o] or (h[c] == h[o] and c < o) for c in chosen)
+
+
 def test_token_permutation_equivariance():
     cfg = SHRUNK["fp8"]
     inp = gen.make_inputs(cfg)

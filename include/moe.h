@@ -66,7 +66,11 @@ typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scor
  * (any weight dtype).  GEMM runs 128-row tiles on the matrix cores and needs bf16 weights with H
  * and I multiples of 64, or FP8 / MXFP4 weights with H and I multiples of 128 (MXFP4: at most
  * 4096); see moe_mode for mode B.  AUTO picks GEMM when it is available and T*k > 4*S, else
- * GEMV.  Asking for GEMM where it is not available fails with MOE_ERR_UNSUPPORTED. */
+ * GEMV.  Asking for GEMM where it is not available fails with MOE_ERR_UNSUPPORTED.
+ * Batch invariance: with a fixed path (GEMV or GEMM, in either mode) a token's output is the
+ * same bits whatever batch it is computed in -- every output element is reduced in a fixed
+ * order whatever other rows share its slot or tile.  AUTO is not batch-invariant: the two
+ * paths round differently (the GEMM path keeps a = silu(g)*u in bf16, the GEMV path in fp32). */
 typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 } moe_path;
 
 /* Expert-FFN arithmetic.  MODE_A: activations kept in bf16/fp32, weights decoded exactly,

@@ -269,6 +269,33 @@ int moe_accumulate_counts(const int32_t* counts, int E, int64_t* hist, void* str
 int moe_plan_slots(const int64_t* hist, int E, int S, int32_t* slot_map, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_refill_slots -- LRU refill of the resident slots after a call (the pages' "full LRU", where
+ * every resident slot is a spare held by the most recently used experts: vLLM-Moet README, the
+ * MoET hybrid measurement matrix, the 4x RTX 5090 row with SPARE=110 and its hit rate).  Each
+ * expert that missed in the call moves into a slot for the next call:
+ *   1. every slot whose expert took rows in the call (counts > 0) gets last_use = step;
+ *   2. the missed experts (counts > 0, slot_map -1) in order of (rows descending, id ascending)
+ *      take the slots not used in the call in order of (last_use ascending, slot ascending),
+ *      as many as both lists allow (empty slots: slot_expert -1 and a last_use below any step);
+ *   3. slot_map, slot_expert and last_use are updated and each moved expert's weights are copied
+ *      from the store into its slot.
+ *   counts       device int32 [E]: the call's rows per expert (moe_permute's counts)
+ *   step         the call's number; increasing from call to call
+ *   slot_map     device int32 [E] in/out (the layer's slot map); slot_expert device int32 [S]
+ *                in/out (its inverse, -1 for an empty slot); last_use device int64 [S] in/out
+ *   store        weights of every expert (store->S == E, slot e = expert e): the backing tier
+ *   slots        the resident weights (slots->S = S <= E), same format and shape
+ *   ws           device workspace of moe_refill_workspace_size(S) bytes, 256-byte aligned; after
+ *                the call it holds the number of moves (int32 at byte 0) and the moves as
+ *                (slot, expert) int32 pairs from byte 256
+ * Deterministic; E <= 1024.  Errors: MOE_ERR_INVALID_ARG / MOE_ERR_WORKSPACE before any launch.
+ * ------------------------------------------------------------------------------------------ */
+size_t moe_refill_workspace_size(int S);
+int moe_refill_slots(const int32_t* counts, int E, long long step, int32_t* slot_map, int32_t* slot_expert,
+                     int64_t* last_use, const moe_weights* store, const moe_weights* slots, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * helpers
  * ------------------------------------------------------------------------------------------ */
 /* Reads the error word at the start of a moe_permute / moe_route_permute / moe_layer workspace: synchronises

@@ -317,6 +317,33 @@ def plan_slots(hist: np.ndarray, S: int) -> np.ndarray:
     return sm
 
 
+def lru_refill(counts, step: int, slot_map, slot_expert, last_use):
+    """LRU refill after a call (the pages' full LRU: every resident slot is a spare held by the
+    most recently used experts -- vLLM-Moet README, MoET hybrid measurement matrix, 4x RTX 5090
+    row).  Slots whose expert took rows in the call are stamped with `step`; the experts that
+    missed (rows > 0, no slot), most rows first (ties: smaller id), move into the slots not used
+    in the call, least recently used first (ties: smaller slot).  Returns the new slot_map,
+    slot_expert, last_use and the moves as (slot, expert) pairs."""
+    counts = [int(c) for c in counts]
+    sm = [int(v) for v in slot_map]
+    se = [int(v) for v in slot_expert]
+    lu = [int(v) for v in last_use]
+    E, S = len(counts), len(se)
+    used = [s for s in range(S) if se[s] >= 0 and counts[se[s]] > 0]
+    free = sorted((s for s in range(S) if s not in used), key=lambda s: (lu[s], s))
+    for s in used:
+        lu[s] = step
+    missed = sorted((e for e in range(E) if counts[e] > 0 and sm[e] < 0), key=lambda e: (-counts[e], e))
+    moves = list(zip(free, missed))
+    for s, e in moves:
+        if se[s] >= 0:
+            sm[se[s]] = -1
+        sm[e] = s
+        se[s] = e
+        lu[s] = step
+    return (np.array(sm, np.int32), np.array(se, np.int32), np.array(lu, np.int64), moves)
+
+
 # ----------------------------------------------------------------------------------------------
 # mode-B activation quantisation mirror (a defined step of the low-precision MFMA path)
 # ----------------------------------------------------------------------------------------------

@@ -62,6 +62,8 @@ _SIGS = {
     "moe_combine_tiers": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_accumulate_counts": (_I, [_P, _I, _P, _P]),
     "moe_plan_slots": (_I, [_P, _I, _I, _P, _P]),
+    "moe_refill_workspace_size": (_Z, [_I]),
+    "moe_refill_slots": (_I, [_P, _I, ctypes.c_longlong, _P, _P, _P, _W, _W, _P, _Z, _P]),
     "moe_layer_workspace_size": (_Z, [_I, _R, _W, _I, _I, _I]),
     "moe_layer": (_I, [_P, _I, _I, _P, _P, _P, _R, _P, _W, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                        _P, _Z, _P]),
@@ -222,6 +224,15 @@ def moe_accumulate_counts(counts, E, hist, stream=None):
 
 def moe_plan_slots(hist, E, S, slot_map, stream=None):
     _check(lib().moe_plan_slots(_ptr(hist), E, S, _ptr(slot_map), _stream(stream)), "moe_plan_slots")
+
+
+def moe_refill_workspace_size(S) -> int:
+    return lib().moe_refill_workspace_size(S)
+
+
+def moe_refill_slots(counts, E, step, slot_map, slot_expert, last_use, store, slots, ws, ws_bytes, stream=None):
+    _check(lib().moe_refill_slots(_ptr(counts), E, step, _ptr(slot_map), _ptr(slot_expert), _ptr(last_use),
+                                  _ref(store), _ref(slots), _ptr(ws), ws_bytes, _stream(stream)), "moe_refill_slots")
 
 
 def moe_layer_workspace_size(T, cfg, w, path, mode, with_router_weights) -> int:

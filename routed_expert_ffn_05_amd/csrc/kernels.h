@@ -90,5 +90,8 @@ hipError_t launch_combine(const float* y, const int32_t* inv, const float* y_b, 
 // hot-set placement (plan.hip)
 hipError_t launch_accumulate_counts(const int32_t* counts, int E, int64_t* hist, hipStream_t st);
 hipError_t launch_plan_slots(const int64_t* hist, int E, int S, int32_t* slot_map, hipStream_t st);
+hipError_t launch_refill(const int32_t* counts, int E, int S, long long step, int32_t* slot_map,
+                         int32_t* slot_expert, int64_t* last_use, int2* plan, int32_t* nplan,
+                         const uint8_t* const src[4], uint8_t* const dst[4], const size_t bytes[4], hipStream_t st);
 
 }  // namespace moe

@@ -632,6 +632,67 @@ int moe_plan_slots(const int64_t* hist, int E, int S, int32_t* slot_map, void* s
   return MOE_OK;
 }
 
+size_t moe_refill_workspace_size(int S) {
+  if (S < 1) return 0;
+  return 256 + align256(size_t(S) * 2 * sizeof(int32_t));
+}
+
+namespace {
+// bytes per slot of the four weight arrays of a descriptor (w_gu, s_gu, w_d, s_d)
+void slot_bytes(const moe_weights* w, size_t b[4]) {
+  auto rowb = [&](int K) -> size_t {
+    switch (w->wdtype) {
+      case MOE_F32: return size_t(K) * 4;
+      case MOE_BF16: return size_t(K) * 2;
+      case MOE_FP8_E4M3_B128: return size_t(K);
+      default: return size_t(K) / 2;
+    }
+  };
+  const size_t N = size_t(2) * w->I;
+  b[0] = N * rowb(w->H);
+  b[2] = size_t(w->H) * rowb(w->I);
+  b[1] = b[3] = 0;
+  if (w->wdtype == MOE_FP8_E4M3_B128) {
+    b[1] = ((N + 127) / 128) * ((size_t(w->H) + 127) / 128) * 4;
+    b[3] = ((size_t(w->H) + 127) / 128) * ((size_t(w->I) + 127) / 128) * 4;
+  } else if (w->wdtype == MOE_MXFP4) {
+    b[1] = N * (w->H / 32);
+    b[3] = size_t(w->H) * (w->I / 32);
+  }
+}
+}  // namespace
+
+int moe_refill_slots(const int32_t* counts, int E, long long step, int32_t* slot_map, int32_t* slot_expert,
+                     int64_t* last_use, const moe_weights* store, const moe_weights* slots, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_INVALID_ARG, "E = %d must be in [1, %d]", E, kMaxE);
+  MOE_TRY(check_weights(store));
+  MOE_TRY(check_weights(slots));
+  if (store->wdtype != slots->wdtype || store->H != slots->H || store->I != slots->I)
+    return fail(MOE_ERR_INVALID_ARG, "store and slots must hold the same format and shape");
+  if (store->S != E) return fail(MOE_ERR_INVALID_ARG, "the store holds every expert: S = %d must equal E = %d", store->S, E);
+  const int S = slots->S;
+  if (S > E) return fail(MOE_ERR_INVALID_ARG, "S = %d above E = %d", S, E);
+  if (!counts || !slot_map || !slot_expert || !last_use) return fail(MOE_ERR_INVALID_ARG, "a NULL pointer");
+  if (!aligned(last_use, 8)) return fail(MOE_ERR_INVALID_ARG, "last_use must be 8-byte aligned");
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < moe_refill_workspace_size(S))
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, moe_refill_workspace_size(S));
+  size_t b[4];
+  slot_bytes(store, b);
+  const uint8_t* src[4] = {static_cast<const uint8_t*>(store->w_gu), static_cast<const uint8_t*>(store->s_gu),
+                           static_cast<const uint8_t*>(store->w_d), static_cast<const uint8_t*>(store->s_d)};
+  uint8_t* dst[4] = {static_cast<uint8_t*>(const_cast<void*>(slots->w_gu)), static_cast<uint8_t*>(const_cast<void*>(slots->s_gu)),
+                     static_cast<uint8_t*>(const_cast<void*>(slots->w_d)), static_cast<uint8_t*>(const_cast<void*>(slots->s_d))};
+  int32_t* nplan = static_cast<int32_t*>(ws);
+  int2* plan = reinterpret_cast<int2*>(static_cast<char*>(ws) + 256);
+  hipError_t e = moe::launch_refill(counts, E, S, step, slot_map, slot_expert, last_use, plan, nplan, src, dst, b,
+                                    as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "refill");
+  return MOE_OK;
+}
+
 int moe_check_device_error(const void* ws, void* stream) {
   if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
   uint32_t word = 0;

@@ -348,6 +348,44 @@ def test_plan_slots_brute_force():
                 assert all(h[c] > h[o] or (h[c] == h[o] and c < o) for c in chosen)
 
 
+def test_lru_refill_worked_example():
+    # E = 6 experts, S = 3 slots holding experts 0, 1 and nothing, last used at steps 5, 3, never.
+    # Call 6 routes rows to experts 0 (2 rows), 3 (4), 4 (1), 5 (4).  By the rule: slot 0 is used
+    # (stamped 6); the missed experts in order are 3, 5 (4 rows each, smaller id first), then 4;
+    # the free slots in order are 2 (never used), then 1 (step 3).  So expert 3 -> slot 2,
+    # expert 5 -> slot 1 (evicting expert 1), expert 4 stays out.
+    sm, se, lu, moves = O.lru_refill([2, 0, 0, 4, 1, 4], 6, [0, 1, -1, -1, -1, -1], [0, 1, -1], [5, 3, -1])
+    assert moves == [(2, 3), (1, 5)]
+    assert sm.tolist() == [0, -1, -1, 2, -1, 1]
+    assert se.tolist() == [0, 5, 3]
+    assert lu.tolist() == [6, 6, 6]
+
+
+def test_lru_refill_invariants():
+    rng = np.random.default_rng(3)
+    for E, S in ((10, 4), (12, 12), (40, 9)):
+        sm = np.full(E, -1, np.int32)
+        se = np.full(S, -1, np.int32)
+        lu = np.full(S, -1, np.int64)
+        for step in range(30):
+            counts = np.zeros(E, np.int64)
+            picks = rng.choice(E, size=rng.integers(1, min(E, 6) + 1), replace=False, p=None)
+            counts[picks] = rng.integers(1, 5, picks.size)
+            missed = [e for e in range(E) if counts[e] > 0 and sm[e] < 0]
+            used = {s for s in range(S) if se[s] >= 0 and counts[se[s]] > 0}
+            nsm, nse, nlu, moves = O.lru_refill(counts, step, sm, se, lu)
+            assert len(moves) == min(len(missed), S - len(used))
+            assert all(e in missed and s not in used for s, e in moves)
+            res = nse[nse >= 0]
+            assert len(set(res.tolist())) == res.size                       # distinct experts
+            assert all(nsm[e] == s for s, e in enumerate(nse) if e >= 0)    # inverse maps
+            assert int((nsm >= 0).sum()) == res.size
+            assert all(nlu[s] == step for s in used)
+            # no slot used in this call lost its expert
+            assert all(nse[s] == se[s] for s in used)
+            sm, se, lu = nsm, nse, nlu
+
+
 def test_token_permutation_equivariance():
     cfg = SHRUNK["fp8"]
     inp = gen.make_inputs(cfg)

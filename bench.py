@@ -12,7 +12,9 @@ The default workload is the bf16 decode layer: T=4 tokens, hidden 4096, 384 expe
 intermediate 1024, top-8 sigmoid routing with renormalised gates.  ``--tiers`` (compact configs)
 adds the second tier to every step: the rows routed to absent experts are permuted over a pool
 holding those experts, computed there, and combined with the resident rows (moe_combine_tiers),
-so the step produces the full layer output.
+so the step produces the full layer output.  ``--lru`` (compact configs) refills the slots after every
+call with the experts that missed (moe_refill_slots, weights copied from a store of every expert);
+``--plan-slots`` places the hot set planned from other batches instead of the seeded map.
 
 The ``roofline`` object describes the dominant kernel (the expert gate/up projection, 2/3 of the
 layer's bytes): algorithmic bytes per launch over its average duration, measured with HIP events
@@ -269,6 +271,18 @@ def run(args):
     w = D.upload_weights(cfg.wdtype, H, I, host_w)
     if not args.cpu_baseline:
         host_w = None
+    lru = bool(args.lru)
+    if lru and (slot_map is None or args.tiers or args.graph_layers or args.plan_slots):
+        raise SystemExit("--lru needs a compact config and runs alone")
+    if lru:
+        # the backing store of every expert (the stand-in for the host tier) and the LRU state;
+        # the slots start with the seeded experts
+        t0 = time.time()
+        store = D.upload_weights(cfg.wdtype, H, I, gen.stack_weights(cfg, range(E)))
+        log(f"generated the store of all {E} experts in {time.time() - t0:.1f}s")
+        w = D.DeviceWeights(cfg.wdtype, S, H, I, *[t.clone() if t is not None else None
+                                                    for t in (w.w_gu, w.s_gu, w.w_d, w.s_d)])
+        lru_init = (slot_map.copy(), np.asarray(slot_expert, np.int32).copy(), np.full(S, -1, np.int64))
     tiers = bool(args.tiers)
     if tiers and args.graph_layers:
         raise SystemExit("--tiers and --graph-layers are not combined")
@@ -323,6 +337,23 @@ def run(args):
     fbytes = moe.moe_expert_ffn_workspace_size(desc, T, k, path, mode)
     fws = D.workspace(fbytes)
     compact = d_sm is not None
+    lru_step = [0]
+    if lru:
+        if args.rotate < args.warmup + args.steps + 8:
+            log("note: --lru over a short rotation revisits batches; use --rotate >= warmup + steps + 8")
+        d_se = D.to_device(lru_init[1])
+        d_lu = D.to_device(lru_init[2])
+        rws = D.workspace(moe.moe_refill_workspace_size(S))
+        w_init = [t.clone() if t is not None else None for t in (w.w_gu, w.s_gu, w.w_d, w.s_d)]
+
+        def lru_reset():
+            d_sm.copy_(D.to_device(lru_init[0]))
+            d_se.copy_(D.to_device(lru_init[1]))
+            d_lu.copy_(D.to_device(lru_init[2]))
+            for a, b in zip((w.w_gu, w.s_gu, w.w_d, w.s_d), w_init):
+                if a is not None:
+                    a.copy_(b)
+            lru_step[0] = 0
     if tiers:
         d_pm = D.to_device(pool_map)
         desc_b = w_pool.desc
@@ -343,7 +374,8 @@ def run(args):
     sp = stream.cuda_stream
 
     def step(i, ev=None, dsc=None, sp=sp):
-        r = i % len(rot)
+        # with the LRU every call takes the next batch of the stream, so that no batch comes back
+        r = (lru_step[0] if lru else i) % len(rot)
         dsc = desc if dsc is None else dsc
         moe.moe_route_permute(d_x[r], xdt, T, H, d_wr, d_lg[r], None, rcfg, d_sm, S, topk_idx, topk_w, counts,
                               off, perm, inv, mc if compact else None, mt if compact else None,
@@ -361,6 +393,9 @@ def run(args):
             moe.moe_combine_tiers(y, inv, y_b, inv_b, topk_w, T, k, H, out, odt, sp)
         else:
             moe.moe_combine(y, inv, topk_w, T, k, H, out, odt, sp)
+        if lru:  # the misses of this call move into slots for the next one
+            moe.moe_refill_slots(counts, E, lru_step[0], d_sm, d_se, d_lu, store.desc, desc, rws, rws.numel(), sp)
+            lru_step[0] += 1
 
     # per-rotation routing statistics (outside the timed region)
     per_rot = []
@@ -424,6 +459,22 @@ def run(args):
         f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s; "
         f"path {'gemm' if gemm else 'gemv'}")
 
+    lru_share = None
+    if lru:
+        # the LRU is deterministic: replay the same calls from the start, untimed, reading the
+        # resident rows (slot_offsets[S]) of each timed call
+        lru_reset()
+        for r in range(len(rot)):
+            step(r)
+        for i in range(args.warmup):
+            step(i)
+        res_rows = 0
+        for i in range(args.steps):
+            step(i)
+            res_rows += int(off[S].item())
+        lru_share = res_rows / (args.steps * T * k)
+        log(f"LRU: resident-row share over the timed calls {lru_share:.3f}")
+
     graph = None
     if args.graph_layers:
         graph = graph_timing(args, step, w, stream, out, T, S, H, I, cfg, D, torch, log)
@@ -432,7 +483,7 @@ def run(args):
 
     # the staged step is moe_layer's own sequence: check one rotation bit for bit (with two tiers
     # the step goes past moe_layer; their identity with one pool is covered by the GPU tests)
-    lay = None if tiers else D.Layer(T=T, H=H, I=I, E=E, k=k, score=cfg.score, renorm=cfg.renorm, xdtype=cfg.xdtype,
+    lay = None if (tiers or lru) else D.Layer(T=T, H=H, I=I, E=E, k=k, score=cfg.score, renorm=cfg.renorm, xdtype=cfg.xdtype,
                   out_dtype=cfg.out_dtype, weights=w, w_router=d_wr, slot_map=d_sm, path=path, mode=mode)
     if lay is not None:
         step(0)
@@ -489,8 +540,9 @@ def run(args):
                    "tokens_per_step": T, "rotations": len(rot), "path": args.path, "mode": args.mode,
                    "layer_algorithmic_GBs": round(layer_gbs, 1),
                    "touched_slots_per_step": round(float(np.mean([p[0] for p in per_rot])), 2),
-                   "resident_row_share": round(float(np.mean([p[1] for p in per_rot])) / (T * k), 4),
+                   "resident_row_share": round(lru_share if lru else float(np.mean([p[1] for p in per_rot])) / (T * k), 4),
                    "slot_map": ("hot set planned on the GPU from 8 untimed batches" if args.plan_slots
+                                else "seeded, then LRU refill after every call" if lru
                                 else "seeded" if slot_map is not None else "all resident"),
                    "timing": (f"HIP graph of {graph['layers']} layers ({graph['weight_copies']} weight copies), "
                               f"per-layer time of its replays" if graph else "eager launches, HIP events")},
@@ -540,6 +592,8 @@ def main(argv=None):
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--mode", default="A", choices=["A", "B"])
     ap.add_argument("--E", type=int, default=None, help="override the expert count of the config")
+    ap.add_argument("--lru", action="store_true",
+                    help="compact configs: after every call, refill the slots with the missed experts (LRU)")
     ap.add_argument("--plan-slots", action="store_true",
                     help="compact configs: resident slots from the hot-set planner instead of the seeded map")
     ap.add_argument("--graph-layers", type=int, default=0,

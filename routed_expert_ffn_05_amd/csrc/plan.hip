@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kPlanThreads) void refill_plan_kernel(const int32_t
 }
 
 // Copy the listed experts' weights from the backing store (slot = expert id) into their slots:
-// four segments per expert (w_gu, s_gu, w_d, s_d), 16-byte copies where the segment allows.
+// four segments per expert (w_gu, s_gu, w_d, s_d), 16-byte copies where addresses and size allow.
 struct RefillSeg {
   const uint8_t* src;
   uint8_t* dst;
@@ -146,7 +146,8 @@ __global__ __launch_bounds__(256) void refill_copy_kernel(const int2* __restrict
     if (!g.bytes) continue;
     const uint8_t* src = g.src + size_t(pe.y) * g.bytes;
     uint8_t* dst = g.dst + size_t(pe.x) * g.bytes;
-    const size_t n16 = (g.bytes % 16 == 0) ? g.bytes / 16 : 0;
+    const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | g.bytes) & 15) == 0;
+    const size_t n16 = vec ? g.bytes / 16 : 0;
     for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256)
       reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
     if (n16 == 0)

@@ -513,7 +513,13 @@ def run(args):
                 "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
                 "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2)}
     if gemm:
+        # mode A runs bf16 MFMA on decoded weights; mode B the block-scaled f8f6f4 MFMA with E4M3
+        # activations, which issues at the FP8 rate whether the weights are E4M3 or E2M1
+        mfma_dt = "fp8" if mode == moe.MOE_MODE_B else "bf16"
         roofline["mfma_tflops"] = round(tflops, 1)
+        roofline["mfma_dtype"] = mfma_dt
+        roofline["mfma_peak"] = MFMA_PEAK_TFLOPS[mfma_dt]
+        roofline["mfma_frac"] = round(tflops / MFMA_PEAK_TFLOPS[mfma_dt], 4)
         roofline["mfma_frac_of_bf16_peak"] = round(tflops / MFMA_PEAK_TFLOPS["bf16"], 4)
 
     cpu = None

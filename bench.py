@@ -509,7 +509,8 @@ def run(args):
     tflops = sum(gate_up_flops(i % len(rot)) for i in range(args.steps)) / (sum(gu_ms) / 1e3) / 1e12
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "moe::gemm::gemm_kernel (gate/up)" if gemm else "moe::gemv::gate_up_kernel",
+                "kernel": (("moe::gemm::gemm_q_kernel" if mode == moe.MOE_MODE_B else "moe::gemm::gemm_kernel")
+                           + " (gate/up)") if gemm else "moe::gemv::gate_up_kernel",
                 "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
                 "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2)}
     if gemm:

@@ -5,16 +5,19 @@
 // weight pool holding the experts tier a lacks, the result is the one-pool layer on the union
 // of the pools, summed in the same order.  Each thread owns four consecutive hidden columns of
 // one token (16-byte loads of the fp32 rows), so the sum order is fixed and the result
-// deterministic.
+// deterministic.  The rows are read once and the output written once, both with non-temporal
+// accesses; a work-group covers a whole 4096-wide token row (1024 threads) where H allows
+// (measured at T = 4096, k = 8, H = 4096: 101 us instead of 116 us with 256 threads and cached
+// accesses).
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kCombThreads = 256;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-template <int ODT>
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __restrict__ y,
+template <int ODT, int THREADS>
+__global__ __launch_bounds__(THREADS) void combine_kernel(const float* __restrict__ y,
                                                                const int32_t* __restrict__ inv,
                                                                const float* __restrict__ y_b,
                                                                const int32_t* __restrict__ inv_b,
@@ -22,7 +25,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
                                                                int k, int H, int cap,
                                                                void* __restrict__ out) {
   const int t = blockIdx.x;
-  const int h = (blockIdx.y * kCombThreads + threadIdx.x) * 4;
+  const int h = (blockIdx.y * THREADS + threadIdx.x) * 4;
   // lanes past H stay active: the positions and gates are read across the wave (readlane), so every
   // lane loads its own; only their row loads and stores are skipped
   const bool live = h < H;
@@ -52,7 +55,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
 #pragma unroll
     for (int u = 0; u < kJ; ++u) {
       v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (src[u]) v[u] = *reinterpret_cast<const float4*>(src[u]);
+      if (src[u]) {
+        const uint4 q = ld_stream16(src[u]);
+        v[u] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w));
+      }
     }
 #pragma unroll
     for (int u = 0; u < kJ; ++u) {
@@ -66,23 +72,29 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __re
   }
   if (!live) return;
   if constexpr (ODT == DT_F32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + size_t(t) * H + h) = acc;
+    const u32x4_t o = {__float_as_uint(acc.x), __float_as_uint(acc.y), __float_as_uint(acc.z), __float_as_uint(acc.w)};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(static_cast<float*>(out) + size_t(t) * H + h));
   } else {
-    uint2 o;
-    o.x = uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16);
-    o.y = uint32_t(f32_to_bf16(acc.z)) | (uint32_t(f32_to_bf16(acc.w)) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + size_t(t) * H + h) = o;
+    const u32x2_t o = {uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16),
+                       uint32_t(f32_to_bf16(acc.z)) | (uint32_t(f32_to_bf16(acc.w)) << 16)};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + size_t(t) * H + h));
   }
 }
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* y_b, const int32_t* inv_b,
                           const float* w, int T, int k, int H, void* out, int odt, hipStream_t st) {
-  dim3 grid(T, (H / 4 + kCombThreads - 1) / kCombThreads), block(kCombThreads);
   const int cap = T * k;
-  if (odt == DT_F32)
-    combine_kernel<DT_F32><<<grid, block, 0, st>>>(y, inv, y_b, inv_b, w, T, k, H, cap, out);
-  else
-    combine_kernel<DT_BF16><<<grid, block, 0, st>>>(y, inv, y_b, inv_b, w, T, k, H, cap, out);
+#define MOE_COMBINE_LAUNCH(N)                                                                  \
+  {                                                                                            \
+    dim3 grid(T, (H / 4 + (N) - 1) / (N)), block(N);                                           \
+    if (odt == DT_F32)                                                                         \
+      combine_kernel<DT_F32, N><<<grid, block, 0, st>>>(y, inv, y_b, inv_b, w, T, k, H, cap, out); \
+    else                                                                                       \
+      combine_kernel<DT_BF16, N><<<grid, block, 0, st>>>(y, inv, y_b, inv_b, w, T, k, H, cap, out); \
+  }
+  if (H >= 4096) MOE_COMBINE_LAUNCH(1024)
+  else MOE_COMBINE_LAUNCH(256)
+#undef MOE_COMBINE_LAUNCH
   return hipGetLastError();
 }
 

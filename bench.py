@@ -18,7 +18,8 @@ call with the experts that missed (moe_refill_slots, weights copied from a store
 
 The ``roofline`` object describes the dominant kernel (the expert gate/up projection, 2/3 of the
 layer's bytes): algorithmic bytes per launch over its average duration, measured with HIP events
-recorded on the launch stream around every timed launch.  ``cpu_baseline`` times the CPU oracle
+recorded on the launch stream around every timed launch (timing-only events, created with
+hipEventDisableSystemFence, so that recording them adds no cache writeback between the kernels).  ``cpu_baseline`` times the CPU oracle
 on a bounded sample of the same workload.
 
 Profiling helpers (no GPU work of their own):
@@ -43,7 +44,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0}
 PROFILES = os.path.join(ROOT, "profiles")
-GATE_UP_SOURCES = ["routed_expert_ffn_05_amd/csrc/gemv_impl.h", "routed_expert_ffn_05_amd/csrc/common.h"]
+# sources of each gate/up kernel: a recorded traffic figure stands only while their hash matches
+GATE_UP_SOURCES = {
+    "gemv": ["routed_expert_ffn_05_amd/csrc/gemv_impl.h", "routed_expert_ffn_05_amd/csrc/common.h"],
+    "gemm": ["routed_expert_ffn_05_amd/csrc/gemm.hip", "routed_expert_ffn_05_amd/csrc/common.h"],
+    "gemm_q": ["routed_expert_ffn_05_amd/csrc/gemm.hip", "routed_expert_ffn_05_amd/csrc/common.h"],
+}
+GATE_UP_KERNELS = {"gemv": "gemv::gate_up_kernel", "gemm": "gemm::gemm_kernel", "gemm_q": "gemm::gemm_q_kernel"}
 
 
 def log(*a):
@@ -99,13 +106,16 @@ def _pmc_per_kernel(d, counter):
     return res
 
 
-def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kernel_key, copy_bytes,
+def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kind, copy_bytes,
                   bytes_per_launch):
+    """PMC summary of the gate/up kernel `kind` (gemv | gemm | gemm_q).  The GEMM template serves
+    both projections; its gate/up instances are the ones whose second template argument is true."""
+    kernel_key = GATE_UP_KERNELS[kind]
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
 
     def pick(dct, key):
-        ks = [k for k in dct if key in k]
+        ks = [k for k in dct if key in k and (kind == "gemv" or k.rstrip().endswith("true>"))]
         if not ks:
             raise SystemExit(f"no kernel matching {key!r} in {sorted(dct)}")
         return dct[ks[0]]
@@ -121,7 +131,7 @@ def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kerne
     kw = pick(write, kernel_key)
     fetch_b = sum(kf) / len(kf) * 1024.0 * (f_factor or 1.0)
     write_b = sum(kw) / len(kw) * 1024.0 * (w_factor or 1.0)
-    lines = ["# HBM traffic of the gate/up GEMV (rocprofv3 PMC)", "",
+    lines = [f"# HBM traffic of the gate/up {'GEMV' if kind == 'gemv' else 'grouped GEMM'} (rocprofv3 PMC)", "",
              f"fetch command: `{command_fetch}`", f"write command: `{command_write}`", "",
              f"kernel: `{kernel_key}`, dispatches: {len(kf)} (FETCH_SIZE), {len(kw)} (WRITE_SIZE)",
              f"copy probe: {copy_bytes} bytes; FETCH_SIZE {copy_f} KiB -> factor {f_factor}; "
@@ -131,15 +141,16 @@ def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kerne
              f"algorithmic bytes per launch (same run): {bytes_per_launch:.0f}",
              "",
              f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
-             f"source_hash: {source_hash(GATE_UP_SOURCES)}"]
+             f"source_hash: {source_hash(GATE_UP_SOURCES[kind])}"]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def recorded_traffic(workload_key):
-    """(traffic bytes per launch, ok) from the committed PMC summary, None if the kernel changed."""
-    p = os.path.join(PROFILES, f"gate_up_gemv_{workload_key}_pmc.md")
+def recorded_traffic(kind, workload_key):
+    """Traffic bytes per launch of gate/up kernel `kind` from the committed PMC summary, None if
+    there is none or the kernel's sources changed since."""
+    p = os.path.join(PROFILES, f"gate_up_{kind}_{workload_key}_pmc.md")
     if not os.path.exists(p):
         return None
     vals = {}
@@ -147,12 +158,66 @@ def recorded_traffic(workload_key):
         if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_hash"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash(GATE_UP_SOURCES):
+    if vals.get("source_hash") != source_hash(GATE_UP_SOURCES[kind]):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+# ---------------------------------------------------------------------------------------------
+# timing-only HIP events
+# ---------------------------------------------------------------------------------------------
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def _hip_runtime():
+    """The HIP runtime library this process already has loaded (torch's), opened by its path so
+    that the handle is the same instance, never a second runtime."""
+    import ctypes
+    with open("/proc/self/maps") as fh:
+        paths = {ln.split()[-1] for ln in fh if "libamdhip64.so" in ln and ln.split()[-1].startswith("/")}
+    if len(paths) != 1:
+        raise SystemExit(f"bench: expected one loaded HIP runtime, found {sorted(paths)}")
+    hip = ctypes.CDLL(paths.pop())
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+class TimingEvent:
+    """A HIP event created with hipEventDisableSystemFence: recording it writes a timestamp when
+    the work before it on the stream is done, without the system-scope cache writeback and
+    invalidation that a default event performs (on this GPU a default event recorded between two
+    kernels adds about 3 us to the step).  Read it only after a device synchronisation."""
+
+    def __init__(self, hip):
+        import ctypes
+        self.hip, self.h = hip, ctypes.c_void_p()
+        rc = hip.hipEventCreateWithFlags(ctypes.byref(self.h), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise SystemExit(f"bench: hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = self.hip.hipEventRecord(self.h, stream.cuda_stream)
+        if rc != 0:
+            raise SystemExit(f"bench: hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise SystemExit(f"bench: hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "h", None) and self.h.value:
+            self.hip.hipEventDestroy(self.h)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -436,7 +501,8 @@ def run(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    hip = _hip_runtime()
+    evs = [(TimingEvent(hip), TimingEvent(hip)) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -505,7 +571,8 @@ def run(args):
         log(f"copy probe: {nb} bytes read and written")
 
     key = f"{cfg.name}_T{T}"
-    traffic = recorded_traffic(key)
+    kind = ("gemm_q" if mode == moe.MOE_MODE_B else "gemm") if gemm else "gemv"
+    traffic = recorded_traffic(kind, key)
     tflops = sum(gate_up_flops(i % len(rot)) for i in range(args.steps)) / (sum(gu_ms) / 1e3) / 1e12
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -552,7 +619,7 @@ def run(args):
                                 else "seeded, then LRU refill after every call" if lru
                                 else "seeded" if slot_map is not None else "all resident"),
                    "timing": (f"HIP graph of {graph['layers']} layers ({graph['weight_copies']} weight copies), "
-                              f"per-layer time of its replays" if graph else "eager launches, HIP events")},
+                              f"per-layer time of its replays" if graph else "eager launches; gate/up timed by fence-free HIP events")},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -612,7 +679,7 @@ def main(argv=None):
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--summarize-kernels", default=None)
     ap.add_argument("--summarize-pmc", nargs=2, default=None)
-    ap.add_argument("--pmc-kernel", default="gemv::gate_up_kernel")
+    ap.add_argument("--pmc-kind", default="gemv", choices=sorted(GATE_UP_KERNELS))
     ap.add_argument("--pmc-copy-bytes", type=int, default=512 << 20)
     ap.add_argument("--pmc-bytes-per-launch", type=float, default=0.0)
     ap.add_argument("--command", nargs="*", default=[])
@@ -623,7 +690,7 @@ def main(argv=None):
         return 0
     if a.summarize_pmc:
         cmds = " ".join(a.command).split(" ;; ")
-        summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], a.out, cmds[0], cmds[-1], a.pmc_kernel,
+        summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], a.out, cmds[0], cmds[-1], a.pmc_kind,
                       a.pmc_copy_bytes, a.pmc_bytes_per_launch)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))

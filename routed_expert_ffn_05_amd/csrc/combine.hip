@@ -6,15 +6,24 @@
 // of the pools, summed in the same order.  Each thread owns four consecutive hidden columns of
 // one token (16-byte loads of the fp32 rows), so the sum order is fixed and the result
 // deterministic.  The rows are read once and the output written once, both with non-temporal
-// accesses; a work-group covers a whole 4096-wide token row (1024 threads) where H allows
-// (measured at T = 4096, k = 8, H = 4096: 101 us instead of 116 us with 256 threads and cached
-// accesses).
+// accesses; a work-group covers a whole 4096-wide token row (1024 threads) where H allows and
+// the batch has at least 64 tokens (measured at T = 4096, k = 8, H = 4096: 101 us instead of
+// 116 us with 256 threads and cached accesses).  Smaller batches are latency-bound: there each
+// 64-thread work-group covers 256 columns of a row (T = 4: the layer step 1.6 us shorter than
+// with one 1024-thread work-group per row).
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#ifndef MOE_COMBINE_WIDE_MIN_T
+#define MOE_COMBINE_WIDE_MIN_T 64     // tokens from which a work-group covers a whole row
+#endif
+#ifndef MOE_COMBINE_SMALL_THREADS
+#define MOE_COMBINE_SMALL_THREADS 64  // threads per work-group below that
+#endif
 
 template <int ODT, int THREADS>
 __global__ __launch_bounds__(THREADS) void combine_kernel(const float* __restrict__ y,
@@ -92,7 +101,8 @@ hipError_t launch_combine(const float* y, const int32_t* inv, const float* y_b, 
     else                                                                                       \
       combine_kernel<DT_BF16, N><<<grid, block, 0, st>>>(y, inv, y_b, inv_b, w, T, k, H, cap, out); \
   }
-  if (H >= 4096) MOE_COMBINE_LAUNCH(1024)
+  if (H >= 4096 && T >= MOE_COMBINE_WIDE_MIN_T) MOE_COMBINE_LAUNCH(1024)
+  else if (T < MOE_COMBINE_WIDE_MIN_T) MOE_COMBINE_LAUNCH(MOE_COMBINE_SMALL_THREADS)
   else MOE_COMBINE_LAUNCH(256)
 #undef MOE_COMBINE_LAUNCH
   return hipGetLastError();

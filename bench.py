@@ -147,6 +147,36 @@ def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kind,
     print("\n".join(lines))
 
 
+def summarize_mfma(d, out, command):
+    """MFMA counters of the grouped GEMMs (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 GRBM_GUI_ACTIVE): per kernel, the
+    matrix work it issued (one MOP = 512 flops), and the share of SIMD cycles its MFMA pipe was
+    busy.  GRBM_GUI_ACTIVE is summed over the 8 XCDs, SQ_VALU_MFMA_BUSY_CYCLES over the 1024
+    SIMDs, so busy / (1024 * GRBM_GUI_ACTIVE / 8) is the pipe's busy fraction."""
+    vals = {}
+    for f in _csvs(d, "*counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "").split("(")[0].replace("void ", "")
+                vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    lines = ["# MFMA counters of the grouped GEMMs (rocprofv3 PMC)", "", f"command: `{command}`", "",
+             "| kernel | dispatches | MOPS bf16 | MOPS f8 | issued TFLOP | active cycles per XCD | MFMA busy |",
+             "|---|---|---|---|---|---|---|"]
+    for name in sorted(vals):
+        v = {c: sum(x) / len(x) for c, x in vals[name].items()}
+        n = len(next(iter(vals[name].values())))
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + v.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+        cyc = v.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024.0 * cyc) if cyc else float("nan")
+        lines.append(f"| {name} | {n} | {v.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0.0):.4g} | "
+                     f"{v.get('SQ_INSTS_VALU_MFMA_MOPS_F8', 0.0):.4g} | {mops * 512 / 1e12:.4f} | {cyc:.4g} | {busy:.3f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def recorded_traffic(kind, workload_key):
     """Traffic bytes per launch of gate/up kernel `kind` from the committed PMC summary, None if
     there is none or the kernel's sources changed since."""
@@ -679,6 +709,7 @@ def main(argv=None):
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--summarize-kernels", default=None)
     ap.add_argument("--summarize-pmc", nargs=2, default=None)
+    ap.add_argument("--summarize-mfma", default=None)
     ap.add_argument("--pmc-kind", default="gemv", choices=sorted(GATE_UP_KERNELS))
     ap.add_argument("--pmc-copy-bytes", type=int, default=512 << 20)
     ap.add_argument("--pmc-bytes-per-launch", type=float, default=0.0)
@@ -687,6 +718,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.summarize_kernels:
         summarize_kernels(a.summarize_kernels, a.out, " ".join(a.command))
+        return 0
+    if a.summarize_mfma:
+        summarize_mfma(a.summarize_mfma, a.out, " ".join(a.command))
         return 0
     if a.summarize_pmc:
         cmds = " ".join(a.command).split(" ;; ")

@@ -24,10 +24,12 @@
 // Gate/up fusion.  The N tile holds 128 gate rows then the 128 matching up rows; wave w reads its
 // 32 MFMA columns as gate rows 16w..16w+15 followed by up rows 16w..16w+15, so lanes l and l+16
 // hold gate and up of the same (row, i) and SiLU(g)*u is formed in registers.
-// Scheduling.  A one-work-group kernel lists the tiles in (slot, M tile, N tile) order; blocks are
-// mapped XCD-major (block b runs on XCD b % 8), so the tiles co-resident on one XCD are the N
-// tiles of a few M tiles of one slot: each activation slice is read from L2 by all N tiles, each
-// weight slice by the few M tiles in flight.
+// Scheduling.  A one-work-group kernel deals the tiles to the eight XCDs (block b runs on XCD
+// b % 8) in units of up to four M tiles of one slot with all their N tiles, so the tiles
+// co-resident on one XCD are the N tiles of a few M tiles of one slot: each activation slice is
+// read from L2 by all N tiles, each weight slice by the M tiles in flight.  Units go out largest
+// first and serpentine over the XCDs, which evens out their work on skewed routing (see
+// schedule_kernel).
 #include <type_traits>
 
 #include "common.h"
@@ -62,13 +64,6 @@ template <int WD> struct BFmt {
   static constexpr int stage_bytes(int ns) { return ns * 32 * AROW + STAGE; }
   static constexpr int nstage(int ns) { return BUDGET / stage_bytes(ns) < 8 ? BUDGET / stage_bytes(ns) : 8; }
 };
-
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-  const int x = b & 7, j = b >> 3;
-  int base = 0;
-  for (int xx = 0; xx < x; ++xx) base += (n - xx + 7) >> 3;
-  return base + j;
-}
 
 // 16 bytes per lane from `src` into LDS at byte address lds + 16*lane (lds wave-uniform).
 // Written as inline assembly so that the compiler's wait insertion does not treat it as aliasing
@@ -114,16 +109,18 @@ template <int WD, bool GATEUP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ off, const int2* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, int T, int k, int K, int N, int I, void* __restrict__ out) {
+    const int32_t* __restrict__ ntiles, int S, int T, int k, int K, int N, int I, void* __restrict__ out) {
   using F = BFmt<WD>;
   __shared__ __align__(16) uint8_t smem[F::BUDGET];
   __shared__ float Ssc[4][64];                                    // FP8 block scales
   __shared__ __align__(16) uint8_t Sfp4[WD == DT_MXFP4 ? BN * kMaxFp4Kb : 16];  // MXFP4 scales
   __shared__ uint8_t rowok[BM];
-  const int n_act = ntiles[0];
-  if (int(blockIdx.x) >= n_act) return;
-  const int2 ent = tiles[xcd_remap(blockIdx.x, n_act)];
+  // tile j = b / 8 of XCD x = b % 8 (the scheduler's per-XCD lists of gridDim.x / 8 entries)
+  const int xcd = blockIdx.x & 7, jt = blockIdx.x >> 3;
+  if (jt >= ntiles[xcd]) return;
+  const int2 ent = tiles[size_t(xcd) * (gridDim.x >> 3) + jt];
   const int s = ent.x, nt = ent.y & 0xFF, mt = ent.y >> 8;
+  if (unsigned(s) >= unsigned(S)) return;  // never taken for the scheduler's entries
   const int cap = T * k;
   const int lo = min(max(off[s], 0), cap), hi = min(max(off[s + 1], lo), cap);
   const int m0 = lo + mt * BM;
@@ -464,7 +461,7 @@ template <int WD, bool GATEUP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint8_t* __restrict__ aq,
     const uint8_t* __restrict__ as, const int32_t* __restrict__ perm, const int32_t* __restrict__ off,
-    const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, int T, int k, int K, int N, int I,
+    const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, int S, int T, int k, int K, int N, int I,
     float* __restrict__ out) {
   static_assert(WD == DT_FP8 || WD == DT_MXFP4, "mode B weights");
   using F = QFmt<WD>;
@@ -473,10 +470,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
   __shared__ __align__(16) uint8_t Sfp4[WD == DT_MXFP4 ? BN * kMaxFp4Kb : 16];    // weight E8M0
   __shared__ __align__(16) uint8_t Sact[BM * kMaxFp4Kb];                          // activation E8M0
   __shared__ uint8_t rowok[BM];
-  const int n_act = ntiles[0];
-  if (int(blockIdx.x) >= n_act) return;
-  const int2 ent = tiles[xcd_remap(blockIdx.x, n_act)];
+  // tile j = b / 8 of XCD x = b % 8 (the scheduler's per-XCD lists of gridDim.x / 8 entries)
+  const int xcd = blockIdx.x & 7, jt = blockIdx.x >> 3;
+  if (jt >= ntiles[xcd]) return;
+  const int2 ent = tiles[size_t(xcd) * (gridDim.x >> 3) + jt];
   const int s = ent.x, nt = ent.y & 0xFF, mt = ent.y >> 8;
+  if (unsigned(s) >= unsigned(S)) return;  // never taken for the scheduler's entries
   const int cap = T * k;
   const int lo = min(max(off[s], 0), cap), hi = min(max(off[s + 1], lo), cap);
   const int m0 = lo + mt * BM;
@@ -744,56 +743,189 @@ __global__ void cast_bf16_kernel(const float* __restrict__ x, uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
-// tile scheduler: M tiles per slot, exclusive scan, then one entry per (slot, M tile, N tile)
-// for both GEMMs.  Entry = {slot, (m_tile << 8) | n_tile}.
+// Tile scheduler (one work-group; S <= 1024, so thread t owns slot t).  Each GEMM block runs one
+// (slot, M tile, N tile) entry {slot, (m_tile << 8) | n_tile}.  The tiles are dealt to the eight
+// XCDs, block b of a launch of 8 * cap blocks running entry j = b / 8 of XCD x = b % 8 (blocks are
+// dealt to the XCDs round robin): tiles[x * cap + j], j < counts[x] (counts[8 + x] for the down
+// GEMM).  With one work-group per CU, each XCD's 32 CUs take its entries in order as they free up.
+//
+// Balanced order.  The unit of work is up to kUnitM consecutive M tiles of one slot with all their
+// N tiles, which an XCD's CUs run side by side, so that the slot's weight slices come from L2 once
+// per unit.  A unit costs about the bytes its tiles move per K step: an M tile of ns 32-row
+// blocks moves ns activation blocks and a weight tile worth 4 of them, so its key is
+// sum(ns + 4) over its M tiles (5 .. 32; 32 = kUnitM full tiles).  Units are sorted by key,
+// largest first (ties in slot order), and dealt serpentine (XCD 0..7, then 7..0, ...), so that the
+// XCDs get similar shares of the bytes and each ends on small units.  Against the (slot, M, N)
+// order in eight equal runs this evens out the XCDs' work on skewed routing: a model of one tile
+// per CU at a time, tile time proportional to those bytes, gives 1.03x the ideal makespan instead
+// of 1.12x on the Zipf prefill batch and 1.10x instead of 1.35x on the 110-slot compact one.
+// Only every slot's last unit can be partial; the others all have key 32.
+// Fallback (the units' table beyond the LDS the host granted, or an XCD's list beyond its
+// capacity): the (slot, M tile, N tile) order cut into eight contiguous runs.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSchedThreads = 1024;
+constexpr int kSchedWaves = kSchedThreads / 64;
+constexpr int kUnitM = 4;                          // M tiles per unit
+constexpr int kKeys = kUnitM * (BM / 32 + 4) + 1;  // unit keys 0 .. 32
+
+__device__ __forceinline__ int serp_xcd(int i) { return ((i >> 3) & 1) ? 7 - (i & 7) : (i & 7); }
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ off, int S,
-                                                                 int cap, int nt_gu, int nt_dn, int max_gu,
-                                                                 int max_dn, int2* __restrict__ tiles_gu,
+                                                                 int cap, int nt_gu, int nt_dn, int slots_gu,
+                                                                 int slots_dn, int umax,
+                                                                 int2* __restrict__ tiles_gu,
                                                                  int2* __restrict__ tiles_dn,
                                                                  int32_t* __restrict__ counts) {
-  extern __shared__ int32_t mbase[];  // [S + 1]
-  __shared__ int32_t wsum[kSchedThreads / 64];
+  extern __shared__ int32_t mbase[];  // [S + 1] M-tile bases; then useq[umax], toff[umax] (balanced)
+  __shared__ int32_t wsum[kSchedWaves];
+  __shared__ int32_t wkey[kSchedWaves][kKeys];  // per-wave key counts, then their bases
+  __shared__ int32_t kbase[kKeys];
+  __shared__ int32_t xcnt[8];
+  __shared__ int32_t nunits, balanced;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int per = (S + kSchedThreads - 1) / kSchedThreads;
-  const int a = tid * per, b = min(S, a + per);
-  int local = 0;
-  for (int s = a; s < b; ++s) {
-    const int lo = min(max(off[s], 0), cap), hi = min(max(off[s + 1], lo), cap);
-    const int mt = (hi - lo + BM - 1) / BM;
-    mbase[s] = mt;
-    local += mt;
+  const int cap_gu = slots_gu >> 3, cap_dn = slots_dn >> 3;
+  // this thread's slot: rows, M tiles, units, key of the last unit
+  int mt = 0, nu = 0, klast = 0;
+  if (tid < S) {
+    const int lo = min(max(off[tid], 0), cap), hi = min(max(off[tid + 1], lo), cap);
+    const int n = hi - lo;
+    mt = (n + BM - 1) / BM;
+    if (mt > 0) {
+      nu = (mt + kUnitM - 1) / kUnitM;
+      const int mtl = mt - kUnitM * (nu - 1);              // M tiles of the last unit
+      const int rl = n - BM * (mt - 1);                    // rows of the slot's last M tile
+      klast = (BM / 32 + 4) * (mtl - 1) + (rl + 31) / 32 + 4;
+    }
   }
-  int incl = local;
+  for (int i = tid; i < kSchedWaves * kKeys; i += kSchedThreads) (&wkey[0][0])[i] = 0;
+  // exclusive scans over slots: M tiles (mbase) and units of key kKeys-1 (f32)
+  const int nfull = nu > 0 ? (nu - 1) + (klast == kKeys - 1 ? 1 : 0) : 0;
+  auto block_scan = [&](int v, int& total) -> int {
+    int incl = v;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) wsum[wid] = incl;
-  __syncthreads();
-  int run = incl - local;
-  for (int w = 0; w < wid; ++w) run += wsum[w];
-  for (int s = a; s < b; ++s) {
-    const int c = mbase[s];
-    mbase[s] = run;
-    run += c;
-  }
-  __syncthreads();
-  int MT = 0;
-  for (int w = 0; w < kSchedThreads / 64; ++w) MT += wsum[w];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int run = incl - v;
+    total = 0;
+    for (int w = 0; w < kSchedWaves; ++w) {
+      if (w < wid) run += wsum[w];
+      total += wsum[w];
+    }
+    __syncthreads();
+    return run;
+  };
+  int MT = 0, nfull_tot = 0;
+  const int mb = block_scan(mt, MT);
+  const int fb = block_scan(nfull, nfull_tot);
+  if (tid < S) mbase[tid] = mb;
   if (tid == 0) mbase[S] = MT;
+  // the last unit of a slot with key below the maximum: its rank among equal keys in lower slots
+  const int ksmall = (nu > 0 && klast < kKeys - 1) ? klast : -1;
+  int rank = 0;
+  {
+    unsigned long long todo = __ballot(ksmall >= 0);
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int lk = __shfl(ksmall, leader);
+      const unsigned long long m = __ballot(ksmall == lk);
+      if (ksmall == lk) rank = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == leader) wkey[wid][lk] = __popcll(m);
+      todo &= ~m;
+    }
+  }
   __syncthreads();
-  // entries: tile L of a GEMM with NT column tiles belongs to the last slot s with
-  // mbase[s] * NT <= L; within the slot, L - mbase[s]*NT = m_tile * NT + n_tile (the N tiles of
-  // one M tile are consecutive: co-resident blocks share the activation rows)
+  if (tid < kKeys) {  // per key: wave bases, key total
+    int run = 0;
+    for (int w = 0; w < kSchedWaves; ++w) {
+      const int c = wkey[w][tid];
+      wkey[w][tid] = run;
+      run += c;
+    }
+    kbase[tid] = run;
+  }
+  __syncthreads();
+  if (tid == 0) {  // key bases, largest key first: the full units, then keys kKeys-2 .. 0
+    int run = nfull_tot;
+    for (int key = kKeys - 2; key >= 0; --key) {
+      const int c = kbase[key];
+      kbase[key] = run;
+      run += c;
+    }
+    kbase[kKeys - 1] = 0;
+    nunits = run;
+    balanced = umax > 0 && run <= umax;
+  }
+  __syncthreads();
+  const int U = nunits;
+  if (balanced) {
+    int32_t* useq = mbase + S + 1;  // sorted units: (unit index << 10) | slot
+    int32_t* toff = useq + umax;    // M-tile offset of a unit in its XCD's list
+    if (tid < S) {
+      const int nf = nu - (ksmall >= 0 ? 1 : 0);
+      for (int i = 0; i < nf; ++i) useq[fb + i] = (i << 10) | tid;
+      if (ksmall >= 0) useq[kbase[ksmall] + wkey[wid][ksmall] + rank] = ((nu - 1) << 10) | tid;
+    }
+    __syncthreads();
+    if (wid < 8) {  // wave x: the units of XCD x (sorted positions 8j + x, or 8j + 7 - x for odd j)
+      const int x = wid;
+      int carry = 0;
+      for (int j0 = 0; 8 * j0 < U; j0 += 64) {
+        const int j = j0 + lane;
+        const int i = 8 * j + ((j & 1) ? 7 - x : x);
+        int m = 0;
+        if (i < U) {
+          const int q = useq[i], s = q & 1023, ui = q >> 10;
+          m = min(kUnitM, (mbase[s + 1] - mbase[s]) - kUnitM * ui);
+        }
+        int incl = m;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_up(incl, o);
+          if (lane >= o) incl += u;
+        }
+        if (i < U) toff[i] = carry + incl - m;
+        carry += __shfl(incl, 63);
+      }
+      if (lane == 0) xcnt[x] = carry;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int x = 0; x < 8; ++x)
+        if (xcnt[x] * nt_gu > cap_gu || xcnt[x] * nt_dn > cap_dn) balanced = 0;
+    }
+    __syncthreads();
+    if (balanced) {
+      for (int i = tid; i < U; i += kSchedThreads) {
+        const int q = useq[i], s = q & 1023, m0 = kUnitM * (q >> 10);
+        const int mu = min(kUnitM, (mbase[s + 1] - mbase[s]) - m0);
+        const int x = serp_xcd(i);
+        for (int g = 0; g < 2; ++g) {
+          const int NT = g ? nt_dn : nt_gu;
+          int2* tl = (g ? tiles_dn : tiles_gu) + size_t(x) * (g ? cap_dn : cap_gu) + size_t(toff[i]) * NT;
+          for (int mm = 0; mm < mu; ++mm)
+            for (int n = 0; n < NT; ++n) tl[mm * NT + n] = make_int2(s, ((m0 + mm) << 8) | n);
+        }
+      }
+      if (tid < 8) {
+        counts[tid] = xcnt[tid] * nt_gu;
+        counts[8 + tid] = xcnt[tid] * nt_dn;
+      }
+      return;
+    }
+  }
+  // fallback: entry L of a GEMM with NT column tiles belongs to the last slot s with
+  // mbase[s] * NT <= L; within the slot, L - mbase[s]*NT = m_tile * NT + n_tile; XCD x takes the
+  // contiguous run of ceil((total - x) / 8) entries after those of XCDs 0 .. x-1
   for (int g = 0; g < 2; ++g) {
     const int NT = g ? nt_dn : nt_gu;
+    const int cx = g ? cap_dn : cap_gu;
     int2* tl = g ? tiles_dn : tiles_gu;
     // the host sized the lists for consistent offsets (sum of rows <= T*k); never write past them
-    const int total = min(MT * NT, g ? max_dn : max_gu);
+    const int total = min(MT * NT, 8 * cx);
     for (int L = tid; L < total; L += kSchedThreads) {
       const int q = L / NT;
       int lo = 0, hi = S - 1;  // last s in [0, S) with mbase[s] <= q
@@ -803,15 +935,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
         else hi = mid - 1;
       }
       const int s = lo;
-      const int mt = mbase[s + 1] - mbase[s];
       const int local2 = L - mbase[s] * NT;
       const int m = local2 / NT, n = local2 - m * NT;
-      tl[L] = make_int2(s, (m << 8) | n);
+      int x = 0, base = 0;
+      while (x < 7 && L >= base + (total - x + 7) / 8) {
+        base += (total - x + 7) / 8;
+        ++x;
+      }
+      tl[size_t(x) * cx + (L - base)] = make_int2(s, (m << 8) | n);
     }
-  }
-  if (tid == 0) {
-    counts[0] = min(MT * nt_gu, max_gu);
-    counts[1] = min(MT * nt_dn, max_dn);
+    if (tid < 8) counts[8 * g + tid] = (total - tid + 7) / 8;
   }
 }
 
@@ -823,21 +956,39 @@ size_t gemm_tiles_max(int T, int k, int S, int nt) {
   return size_t(mt) * nt;
 }
 
+// eight per-XCD lists, each an eighth of the bound plus one unit of kUnitM M tiles (the balanced
+// order can put up to a unit more than an even share on one XCD)
+size_t gemm_tile_slots(int T, int k, int S, int nt) {
+  const size_t m = gemm_tiles_max(T, k, S, nt);
+  return m == 0 ? 0 : ((m + 7) / 8 + size_t(gemm::kUnitM) * nt) * 8;
+}
+
 int gemm_nt_gate_up(int I) { return (I + gemm::BN / 2 - 1) / (gemm::BN / 2); }
 int gemm_nt_down(int H) { return (H + gemm::BN - 1) / gemm::BN; }
 
 hipError_t launch_gemm_schedule(const GemmArgs& g, hipStream_t st) {
-  const size_t lds = sizeof(int32_t) * size_t(g.S + 1);
   const int ngu = gemm_nt_gate_up(g.I), ndn = gemm_nt_down(g.H);
+  // the balanced order keeps two words per unit in LDS (units <= M tiles <= the bound below);
+  // beyond the LDS budget the scheduler falls back to contiguous runs
+  constexpr size_t kDynLdsMax = 150 * 1024;
+  const size_t base = sizeof(int32_t) * size_t(g.S + 1);
+  const size_t umax = gemm_tiles_max(g.T, g.k, g.S, 1);
+  const bool fits = base + 2 * sizeof(int32_t) * umax <= kDynLdsMax;
+  const size_t lds = fits ? base + 2 * sizeof(int32_t) * umax : base;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm::schedule_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
   gemm::schedule_kernel<<<1, gemm::kSchedThreads, lds, st>>>(
-      g.off, g.S, g.T * g.k, ngu, ndn, int(gemm_tiles_max(g.T, g.k, g.S, ngu)), int(gemm_tiles_max(g.T, g.k, g.S, ndn)),
-      g.tiles_gu, g.tiles_dn, g.counts);
+      g.off, g.S, g.T * g.k, ngu, ndn, int(gemm_tile_slots(g.T, g.k, g.S, ngu)),
+      int(gemm_tile_slots(g.T, g.k, g.S, ndn)), fits ? int(umax) : 0, g.tiles_gu, g.tiles_dn, g.counts);
   return hipGetLastError();
 }
 
 template <int WD>
 static hipError_t gate_up_t(const GemmArgs& g, hipStream_t st) {
-  const size_t grid = gemm_tiles_max(g.T, g.k, g.S, gemm_nt_gate_up(g.I));
+  const size_t grid = gemm_tile_slots(g.T, g.k, g.S, gemm_nt_gate_up(g.I));
   if (grid == 0) return hipSuccess;
   const void* x = g.x;
   if (g.xdt == DT_F32) {  // the matrix cores read bf16: round the activations once
@@ -848,37 +999,37 @@ static hipError_t gate_up_t(const GemmArgs& g, hipStream_t st) {
   }
   gemm::gemm_kernel<WD, true><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
       static_cast<const uint8_t*>(g.w_gu), g.s_gu, static_cast<const uint16_t*>(x), g.perm, g.off, g.tiles_gu,
-      g.counts, g.T, g.k, g.H, 2 * g.I, g.I, g.a);
+      g.counts, g.S, g.T, g.k, g.H, 2 * g.I, g.I, g.a);
   return hipGetLastError();
 }
 
 template <int WD>
 static hipError_t down_t(const GemmArgs& g, hipStream_t st) {
-  const size_t grid = gemm_tiles_max(g.T, g.k, g.S, gemm_nt_down(g.H));
+  const size_t grid = gemm_tile_slots(g.T, g.k, g.S, gemm_nt_down(g.H));
   if (grid == 0) return hipSuccess;
   gemm::gemm_kernel<WD, false><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
       static_cast<const uint8_t*>(g.w_d), g.s_d, static_cast<const uint16_t*>(g.a), nullptr, g.off, g.tiles_dn,
-      g.counts + 1, g.T, g.k, g.I, g.H, g.I, g.y);
+      g.counts + 8, g.S, g.T, g.k, g.I, g.H, g.I, g.y);
   return hipGetLastError();
 }
 
 template <int WD>
 static hipError_t gate_up_q_t(const GemmArgs& g, hipStream_t st) {
-  const size_t grid = gemm_tiles_max(g.T, g.k, g.S, gemm_nt_gate_up(g.I));
+  const size_t grid = gemm_tile_slots(g.T, g.k, g.S, gemm_nt_gate_up(g.I));
   if (grid == 0) return hipSuccess;
   gemm::gemm_q_kernel<WD, true><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-      static_cast<const uint8_t*>(g.w_gu), g.s_gu, g.xq, g.xs, g.perm, g.off, g.tiles_gu, g.counts, g.T, g.k,
-      g.H, 2 * g.I, g.I, static_cast<float*>(g.a));
+      static_cast<const uint8_t*>(g.w_gu), g.s_gu, g.xq, g.xs, g.perm, g.off, g.tiles_gu, g.counts, g.S, g.T,
+      g.k, g.H, 2 * g.I, g.I, static_cast<float*>(g.a));
   return hipGetLastError();
 }
 
 template <int WD>
 static hipError_t down_q_t(const GemmArgs& g, hipStream_t st) {
-  const size_t grid = gemm_tiles_max(g.T, g.k, g.S, gemm_nt_down(g.H));
+  const size_t grid = gemm_tile_slots(g.T, g.k, g.S, gemm_nt_down(g.H));
   if (grid == 0) return hipSuccess;
   gemm::gemm_q_kernel<WD, false><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-      static_cast<const uint8_t*>(g.w_d), g.s_d, g.aq, g.as, nullptr, g.off, g.tiles_dn, g.counts + 1, g.T, g.k,
-      g.I, g.H, g.I, g.y);
+      static_cast<const uint8_t*>(g.w_d), g.s_d, g.aq, g.as, nullptr, g.off, g.tiles_dn, g.counts + 8, g.S,
+      g.T, g.k, g.I, g.H, g.I, g.y);
   return hipGetLastError();
 }
 

@@ -64,9 +64,11 @@ struct GemmArgs {
   uint8_t* as;          // [T*k, I/32]
   int2* tiles_gu;       // tile lists written by the scheduler
   int2* tiles_dn;
-  int32_t* counts;      // [2]: tiles of each GEMM
+  int32_t* counts;      // [16]: tiles per XCD of the gate/up GEMM, then of the down GEMM
 };
 size_t gemm_tiles_max(int T, int k, int S, int nt);
+// entries of a GEMM's tile list (eight per-XCD lists of gemm_tile_slots / 8) = its launch grid
+size_t gemm_tile_slots(int T, int k, int S, int nt);
 int gemm_nt_gate_up(int I);
 int gemm_nt_down(int H);
 hipError_t launch_gemm_schedule(const GemmArgs& g, hipStream_t st);

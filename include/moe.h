@@ -70,7 +70,11 @@ typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scor
  * Batch invariance: with a fixed path (GEMV or GEMM, in either mode) a token's output is the
  * same bits whatever batch it is computed in -- every output element is reduced in a fixed
  * order whatever other rows share its slot or tile.  AUTO is not batch-invariant: the two
- * paths round differently (the GEMM path keeps a = silu(g)*u in bf16, the GEMV path in fp32). */
+ * paths round differently (the GEMM path keeps a = silu(g)*u in bf16, the GEMV path in fp32).
+ * GEMM tile order: the tiles are dealt to the GPU's eight XCDs in cost-sorted units of a slot's
+ * M tiles; the environment variable MOE_GEMM_TILE_ORDER=contiguous (read at every call) selects
+ * the plain (slot, M tile, N tile) order in eight contiguous runs instead.  The order changes
+ * only which compute unit runs a tile, never the arithmetic: both give the same bits. */
 typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 } moe_path;
 
 /* Expert-FFN arithmetic.  MODE_A: activations kept in bf16/fp32, weights decoded exactly,

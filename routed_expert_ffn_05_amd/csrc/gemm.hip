@@ -30,6 +30,8 @@
 // read from L2 by all N tiles, each weight slice by the M tiles in flight.  Units go out largest
 // first and serpentine over the XCDs, which evens out their work on skewed routing (see
 // schedule_kernel).
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "common.h"
@@ -975,7 +977,10 @@ hipError_t launch_gemm_schedule(const GemmArgs& g, hipStream_t st) {
   constexpr size_t kDynLdsMax = 150 * 1024;
   const size_t base = sizeof(int32_t) * size_t(g.S + 1);
   const size_t umax = gemm_tiles_max(g.T, g.k, g.S, 1);
-  const bool fits = base + 2 * sizeof(int32_t) * umax <= kDynLdsMax;
+  // MOE_GEMM_TILE_ORDER=contiguous asks for the fallback order (same results, other placement)
+  const char* order = std::getenv("MOE_GEMM_TILE_ORDER");
+  const bool contiguous = order && std::strcmp(order, "contiguous") == 0;
+  const bool fits = !contiguous && base + 2 * sizeof(int32_t) * umax <= kDynLdsMax;
   const size_t lds = fits ? base + 2 * sizeof(int32_t) * umax : base;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm::schedule_kernel,

@@ -12,25 +12,6 @@ namespace moe {
 
 constexpr int kQThreads = 256;
 
-// nearest-even E4M3 (e4m3fn) code of y, saturating at +-448 (finite y)
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  if (!(a < 448.0f)) return sign | 0x7Eu;
-  if (a == 0.0f) return sign;
-  int e;
-  (void)frexpf(a, &e);
-  e -= 1;  // a in [2^e, 2^(e+1))
-  if (e < -6) return sign | uint32_t(rintf(a * 512.0f));  // multiples of 2^-9 (8 -> 2^-6, code 0x08)
-  int m = int(rintf(ldexpf(a, 3 - e)));                   // 8 .. 16
-  if (m == 16) {
-    m = 8;
-    ++e;
-  }
-  const uint32_t code = (uint32_t(e + 7) << 3) | uint32_t(m - 8);
-  return sign | (code > 0x7Eu ? 0x7Eu : code);
-}
-
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const int e = (c >> 3) & 15, m = c & 7;
   const float v = e == 0 ? ldexpf(float(m), -9) : ldexpf(float(8 + m), e - 10);
@@ -63,12 +44,7 @@ __global__ __launch_bounds__(kQThreads) void act_quant_kernel(const void* __rest
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
-  int X = 0;
-  if (amax > 0.0f) {
-    int ex;
-    (void)frexpf(amax, &ex);
-    X = max(ex - 9, -127);  // floor(log2 amax) - 8, kept within E8M0
-  }
+  const int X = mx_e4m3_exponent(amax);
   const float inv = ldexpf(1.0f, -X);
   uint32_t c[8];
 #pragma unroll

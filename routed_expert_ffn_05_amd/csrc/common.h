@@ -59,6 +59,36 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Mode B activation quantisation (OCP MX rule with E4M3 elements), shared by the quantisation
+// kernel and the gate/up GEMM's epilogue so both give the same bits.
+// Nearest-even E4M3 (e4m3fn) code of a finite y, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a == 0.0f) return sign;
+  int e;
+  (void)frexpf(a, &e);
+  e -= 1;  // a in [2^e, 2^(e+1))
+  if (e < -6) return sign | uint32_t(rintf(a * 512.0f));  // multiples of 2^-9 (8 -> 2^-6, code 0x08)
+  int m = int(rintf(ldexpf(a, 3 - e)));                   // 8 .. 16
+  if (m == 16) {
+    m = 8;
+    ++e;
+  }
+  const uint32_t code = (uint32_t(e + 7) << 3) | uint32_t(m - 8);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// Shared exponent X of a 32-element block with largest magnitude amax: floor(log2 amax) - 8
+// (E4M3's largest exponent is 8), 0 for an all-zero block, kept within E8M0 (>= -127).
+__device__ __forceinline__ int mx_e4m3_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int ex;
+  (void)frexpf(amax, &ex);
+  return max(ex - 9, -127);
+}
+
 // ---------------------------------------------------------------------------------------------
 // wave-level reductions (64 lanes)
 // ---------------------------------------------------------------------------------------------

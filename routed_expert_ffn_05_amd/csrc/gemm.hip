@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 // two); operand lanes: lane (r, h) holds 8-bit K granules h and 2+h (16 elements each) of its 64,
 // or 4-bit K [32h, 32h+32);
 // lane r+32b supplies the scale of K block b of row (column) r.
-// GATEUP = true:  A = quantised x rows (through perm), out a (fp32, quantised again before down)
+// GATEUP = true:  A = quantised x rows (through perm), out a quantised (aq_out, as_out) for down
 // GATEUP = false: A = quantised a rows (positions),    out y (fp32)
 // ---------------------------------------------------------------------------------------------
 template <int WD> struct QFmt {
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint8_t* __restrict__ aq,
     const uint8_t* __restrict__ as, const int32_t* __restrict__ perm, const int32_t* __restrict__ off,
     const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, int S, int T, int k, int K, int N, int I,
-    float* __restrict__ out) {
+    float* __restrict__ out, uint8_t* __restrict__ aq_out, uint8_t* __restrict__ as_out) {
   static_assert(WD == DT_FP8 || WD == DT_MXFP4, "mode B weights");
   using F = QFmt<WD>;
   __shared__ __align__(16) uint8_t smem[F::BUDGET];
@@ -713,19 +713,55 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
     }
     wait_vmcnt<0>();
 
+    if constexpr (GATEUP) {
+      // a = silu(g) * u of the tile (rows x 128 columns; I is a multiple of 128 here) goes through
+      // LDS and leaves quantised, per row and 32 columns, by the rule of the quantisation kernel
+      // (the down projection's input): one write of 1 + 1/32 bytes per element instead of an fp32
+      // store and a second pass over it
+      float* at = reinterpret_cast<float*>(smem);  // [BM][128] fp32 (64 KiB of the stages)
+      __syncthreads();  // every wave's direct loads have landed and its stage reads are done
 #pragma unroll
-    for (int ms = 0; ms < NS; ++ms) {
+      for (int ms = 0; ms < NS; ++ms) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        const float v = acc[ms][r];
-        if constexpr (GATEUP) {
+        for (int r = 0; r < 16; ++r) {
+          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+          const float v = acc[ms][r];
           const float o = __shfl_xor(v, 16);
-          if (ln < 16 && m < rows) {
-            const int i = n0 + 16 * wv + ln;
-            if (i < I) out[size_t(m0 + m) * I + i] = rowok[m] ? silu(v) * o : 0.0f;
-          }
-        } else {
+          if (ln < 16 && m < rows) at[m * 128 + 16 * wv + ln] = rowok[m] ? silu(v) * o : 0.0f;
+        }
+      }
+      __syncthreads();
+      const int KB = I >> 5;
+      // four lanes per 32-column block (eight columns each), the block maximum by two lane swaps;
+      // groups of four lanes are active together (rows * 16 is a multiple of 4)
+      for (int t = tid; t < rows * 16; t += kThreads) {
+        const int m = t >> 4, blk = (t >> 2) & 3, part = t & 3;
+        const float4 p = *reinterpret_cast<const float4*>(at + m * 128 + blk * 32 + part * 8);
+        const float4 q = *reinterpret_cast<const float4*>(at + m * 128 + blk * 32 + part * 8 + 4);
+        const float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        const int X = mx_e4m3_exponent(amax);
+        const float inv = ldexpf(1.0f, -X);
+        uint32_t c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = e4m3_code(v[i] * inv);
+        uint2 o2;
+        o2.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        o2.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        *reinterpret_cast<uint2*>(aq_out + size_t(m0 + m) * I + n0 + blk * 32 + part * 8) = o2;
+        if (part == 0) as_out[size_t(m0 + m) * KB + (n0 >> 5) + blk] = uint8_t(X + 127);
+      }
+    } else {
+#pragma unroll
+      for (int ms = 0; ms < NS; ++ms) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+          const float v = acc[ms][r];
           const int h = n0 + 32 * wv + ln;
           if (m < rows && h < N) __builtin_nontemporal_store(v, out + size_t(m0 + m) * N + h);  // as in mode A
         }
@@ -1026,7 +1062,7 @@ static hipError_t gate_up_q_t(const GemmArgs& g, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   gemm::gemm_q_kernel<WD, true><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
       static_cast<const uint8_t*>(g.w_gu), g.s_gu, g.xq, g.xs, g.perm, g.off, g.tiles_gu, g.counts, g.S, g.T,
-      g.k, g.H, 2 * g.I, g.I, static_cast<float*>(g.a));
+      g.k, g.H, 2 * g.I, g.I, nullptr, g.aq, g.as);
   return hipGetLastError();
 }
 
@@ -1036,7 +1072,7 @@ static hipError_t down_q_t(const GemmArgs& g, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   gemm::gemm_q_kernel<WD, false><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
       static_cast<const uint8_t*>(g.w_d), g.s_d, g.aq, g.as, nullptr, g.off, g.tiles_dn, g.counts + 8, g.S,
-      g.T, g.k, g.I, g.H, g.I, g.y);
+      g.T, g.k, g.I, g.H, g.I, g.y, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ struct GemmArgs {
   void* xb;             // [T, H] bf16 scratch: fp32 activations rounded once for the matrix cores
   const int32_t* perm;
   const int32_t* off;
-  void* a;              // [T*k, I] bf16 (mode A) or fp32 (mode B)
+  void* a;              // [T*k, I] bf16 (mode A); unused in mode B, which writes aq/as directly
   float* y;             // [T*k, H] fp32
   // mode B: E4M3 codes and E8M0 scales (per row and 32 K) of x and a
   uint8_t* xq;          // [T, H]

@@ -375,9 +375,8 @@ int moe_expert_gate_up(const moe_weights* w, const void* x, int x_dtype, int T, 
     if (mode == MOE_MODE_B)  // E4M3 codes + E8M0 scales of x
       e = moe::launch_act_quant(x, x_dtype, T, w->H, nullptr, g.xq, g.xs, nullptr, 0, st);
     if (e == hipSuccess) e = moe::launch_gemm_schedule(g, st);
+    // mode B: the gate/up GEMM writes a already quantised (aq, as) for the down GEMM
     if (e == hipSuccess) e = mode == MOE_MODE_B ? moe::launch_gemm_gate_up_q(g, st) : moe::launch_gemm_gate_up(g, st);
-    if (e == hipSuccess && mode == MOE_MODE_B)  // and of a (fp32), over the n_res resident rows
-      e = moe::launch_act_quant(g.a, MOE_F32, R, w->I, slot_offsets + w->S, g.aq, g.as, nullptr, 0, st);
     if (e != hipSuccess) return hip_fail(e, "gate/up GEMM");
     return MOE_OK;
   }

@@ -408,24 +408,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
     // ---- epilogue: accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4 of its row block,
     // column l%32
+    if constexpr (GATEUP) {
+      // a = silu(g) * u in bf16 goes through LDS so that it leaves in whole 16-byte pieces per
+      // lane (the accumulator layout gives 2-byte pieces, 16 lanes to a row segment)
+      uint16_t* at = reinterpret_cast<uint16_t*>(smem);  // [BM][128] bf16
+      __syncthreads();  // every wave's direct loads have landed and its stage reads are done
 #pragma unroll
-    for (int ms = 0; ms < NS; ++ms) {
+      for (int ms = 0; ms < NS; ++ms) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        const float v = acc[ms][r];
-        if constexpr (GATEUP) {
+        for (int r = 0; r < 16; ++r) {
+          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+          const float v = acc[ms][r];
           const float o = __shfl_xor(v, 16);
-          if (ln < 16 && m < rows) {
-            const int i = n0 + 16 * wv + ln;
-            if (i < I)
-              static_cast<uint16_t*>(out)[size_t(m0 + m) * I + i] = rowok[m] ? f32_to_bf16(silu(v) * o) : uint16_t(0);
-          }
-        } else {
+          if (ln < 16 && m < rows) at[m * 128 + 16 * wv + ln] = rowok[m] ? f32_to_bf16(silu(v) * o) : uint16_t(0);
+        }
+      }
+      __syncthreads();
+      const int ncol = min(128, I - n0);  // columns of this tile (a multiple of 8)
+      for (int t = tid; t < rows * 16; t += kThreads) {
+        const int m = t >> 4, c8 = (t & 15) * 8;
+        if (c8 < ncol)
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + size_t(m0 + m) * I + n0 + c8) =
+              *reinterpret_cast<const uint4*>(at + m * 128 + c8);
+      }
+    } else {
+#pragma unroll
+      for (int ms = 0; ms < NS; ++ms) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
           const int h = n0 + 32 * wv + ln;
           // y is read once, by the combine, long after: streamed past the caches (down GEMM 5 %
           // faster at the prefill shapes than with cached stores)
-          if (m < rows && h < N) __builtin_nontemporal_store(v, static_cast<float*>(out) + size_t(m0 + m) * N + h);
+          if (m < rows && h < N)
+            __builtin_nontemporal_store(acc[ms][r], static_cast<float*>(out) + size_t(m0 + m) * N + h);
         }
       }
     }

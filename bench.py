@@ -610,6 +610,12 @@ def run(args):
                            + " (gate/up)") if gemm else "moe::gemv::gate_up_kernel",
                 "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
                 "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2)}
+    if traffic is not None:
+        # the counters' HBM bytes over the same live launch time: within 10 % of `achieved` when
+        # the kernel moves about its algorithmic bytes, above it when it re-reads
+        tgbs = traffic / (float(np.mean(gu_ms)) / 1e3) / 1e9
+        roofline["traffic_GBs"] = round(tgbs, 1)
+        roofline["traffic_vs_algorithmic"] = round(traffic / (sum(gu_bytes) / len(gu_bytes)), 3)
     if gemm:
         # mode A runs bf16 MFMA on decoded weights; mode B the block-scaled f8f6f4 MFMA with E4M3
         # activations, which issues at the FP8 rate whether the weights are E4M3 or E2M1

@@ -110,24 +110,24 @@ __host__ __device__ constexpr size_t row_bytes(int K) {
 template <int WD, bool GATEUP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint16_t* __restrict__ act,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ off, const int2* __restrict__ tiles,
+    const int32_t* __restrict__ perm, const int4* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, int S, int T, int k, int K, int N, int I, void* __restrict__ out) {
   using F = BFmt<WD>;
   __shared__ __align__(16) uint8_t smem[F::BUDGET];
   __shared__ float Ssc[4][64];                                    // FP8 block scales
   __shared__ __align__(16) uint8_t Sfp4[WD == DT_MXFP4 ? BN * kMaxFp4Kb : 16];  // MXFP4 scales
   __shared__ uint8_t rowok[BM];
-  // tile j = b / 8 of XCD x = b % 8 (the scheduler's per-XCD lists of gridDim.x / 8 entries)
+  // tile j = b / 8 of XCD x = b % 8 (the scheduler's per-XCD lists of gridDim.x / 8 entries); the
+  // count and the entry are loaded together (the entry slot exists for every block), and the entry
+  // carries the tile's first row and row count, so no further index load precedes the operands
   const int xcd = blockIdx.x & 7, jt = blockIdx.x >> 3;
-  if (jt >= ntiles[xcd]) return;
-  const int2 ent = tiles[size_t(xcd) * (gridDim.x >> 3) + jt];
-  const int s = ent.x, nt = ent.y & 0xFF, mt = ent.y >> 8;
-  if (unsigned(s) >= unsigned(S)) return;  // never taken for the scheduler's entries
+  const int ncnt = ntiles[xcd];
+  const int4 ent = tiles[size_t(xcd) * (gridDim.x >> 3) + jt];
+  if (jt >= ncnt) return;
+  const int s = ent.x, m0 = ent.y, rows = ent.z, nt = ent.w;
   const int cap = T * k;
-  const int lo = min(max(off[s], 0), cap), hi = min(max(off[s + 1], lo), cap);
-  const int m0 = lo + mt * BM;
-  const int rows = min(BM, hi - m0);
-  if (rows <= 0) return;
+  // never taken for the scheduler's entries
+  if (unsigned(s) >= unsigned(S) || rows <= 0 || rows > BM || m0 < 0 || m0 + rows > cap) return;
   const int nsub = (rows + 31) >> 5;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, kh = lane >> 5;
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   const bool fp4_async = WD == DT_MXFP4 && KB32 % 16 == 0;
   const int gpr = fp4_async ? KB32 >> 4 : 1;
   // rows r and r + D start in the same bank: D = 64 dwords over the row's dwords, made coprime
-  const int fp4_d = fp4_async ? 16 / (gpr & -gpr < 16 ? gpr & -gpr : 16) : 1;
+  const int fp4_d = fp4_async ? 16 / ((gpr & -gpr) < 16 ? (gpr & -gpr) : 16) : 1;
   auto fp4_key = [&](int r) -> int { return fp4_async ? (r / fp4_d) % gpr : 0; };
   if constexpr (WD == DT_MXFP4) {
     if (!fp4_async) {
@@ -480,8 +480,8 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 template <int WD, bool GATEUP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint8_t* __restrict__ aq,
-    const uint8_t* __restrict__ as, const int32_t* __restrict__ perm, const int32_t* __restrict__ off,
-    const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, int S, int T, int k, int K, int N, int I,
+    const uint8_t* __restrict__ as, const int32_t* __restrict__ perm,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, int S, int T, int k, int K, int N, int I,
     float* __restrict__ out, uint8_t* __restrict__ aq_out, uint8_t* __restrict__ as_out) {
   static_assert(WD == DT_FP8 || WD == DT_MXFP4, "mode B weights");
   using F = QFmt<WD>;
@@ -490,17 +490,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
   __shared__ __align__(16) uint8_t Sfp4[WD == DT_MXFP4 ? BN * kMaxFp4Kb : 16];    // weight E8M0
   __shared__ __align__(16) uint8_t Sact[BM * kMaxFp4Kb];                          // activation E8M0
   __shared__ uint8_t rowok[BM];
-  // tile j = b / 8 of XCD x = b % 8 (the scheduler's per-XCD lists of gridDim.x / 8 entries)
+  // tile j = b / 8 of XCD x = b % 8 (the scheduler's per-XCD lists of gridDim.x / 8 entries); the
+  // count and the entry are loaded together (the entry slot exists for every block), and the entry
+  // carries the tile's first row and row count, so no further index load precedes the operands
   const int xcd = blockIdx.x & 7, jt = blockIdx.x >> 3;
-  if (jt >= ntiles[xcd]) return;
-  const int2 ent = tiles[size_t(xcd) * (gridDim.x >> 3) + jt];
-  const int s = ent.x, nt = ent.y & 0xFF, mt = ent.y >> 8;
-  if (unsigned(s) >= unsigned(S)) return;  // never taken for the scheduler's entries
+  const int ncnt = ntiles[xcd];
+  const int4 ent = tiles[size_t(xcd) * (gridDim.x >> 3) + jt];
+  if (jt >= ncnt) return;
+  const int s = ent.x, m0 = ent.y, rows = ent.z, nt = ent.w;
   const int cap = T * k;
-  const int lo = min(max(off[s], 0), cap), hi = min(max(off[s + 1], lo), cap);
-  const int m0 = lo + mt * BM;
-  const int rows = min(BM, hi - m0);
-  if (rows <= 0) return;
+  // never taken for the scheduler's entries
+  if (unsigned(s) >= unsigned(S) || rows <= 0 || rows > BM || m0 < 0 || m0 + rows > cap) return;
   const int nsub = (rows + 31) >> 5;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, kh = lane >> 5;
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
   const int KB32 = K >> 5;
   const bool sc_async = KB32 % 16 == 0;
   const int gpr = sc_async ? KB32 >> 4 : 1;
-  const int sc_d = sc_async ? 16 / (gpr & -gpr < 16 ? gpr & -gpr : 16) : 1;
+  const int sc_d = sc_async ? 16 / ((gpr & -gpr) < 16 ? (gpr & -gpr) : 16) : 1;
   auto sc_key = [&](int r) -> int { return sc_async ? (r / sc_d) % gpr : 0; };
   auto sc_index = [&](int r, int kb) -> int {
     if (!sc_async) return r * KB32 + kb;
@@ -800,7 +800,7 @@ __global__ void cast_bf16_kernel(const float* __restrict__ x, uint16_t* __restri
 
 // ---------------------------------------------------------------------------------------------
 // Tile scheduler (one work-group; S <= 1024, so thread t owns slot t).  Each GEMM block runs one
-// (slot, M tile, N tile) entry {slot, (m_tile << 8) | n_tile}.  The tiles are dealt to the eight
+// (slot, M tile, N tile) entry {slot, first row, rows, n_tile}.  The tiles are dealt to the eight
 // XCDs, block b of a launch of 8 * cap blocks running entry j = b / 8 of XCD x = b % 8 (blocks are
 // dealt to the XCDs round robin): tiles[x * cap + j], j < counts[x] (counts[8 + x] for the down
 // GEMM).  With one work-group per CU, each XCD's 32 CUs take its entries in order as they free up.
@@ -829,8 +829,8 @@ __device__ __forceinline__ int serp_xcd(int i) { return ((i >> 3) & 1) ? 7 - (i 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ off, int S,
                                                                  int cap, int nt_gu, int nt_dn, int slots_gu,
                                                                  int slots_dn, int umax,
-                                                                 int2* __restrict__ tiles_gu,
-                                                                 int2* __restrict__ tiles_dn,
+                                                                 int4* __restrict__ tiles_gu,
+                                                                 int4* __restrict__ tiles_dn,
                                                                  int32_t* __restrict__ counts) {
   extern __shared__ int32_t mbase[];  // [S + 1] M-tile bases; then useq[umax], toff[umax] (balanced)
   __shared__ int32_t wsum[kSchedWaves];
@@ -959,11 +959,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
         const int q = useq[i], s = q & 1023, m0 = kUnitM * (q >> 10);
         const int mu = min(kUnitM, (mbase[s + 1] - mbase[s]) - m0);
         const int x = serp_xcd(i);
+        const int lo = min(max(off[s], 0), cap), hi = min(max(off[s + 1], lo), cap);
         for (int g = 0; g < 2; ++g) {
           const int NT = g ? nt_dn : nt_gu;
-          int2* tl = (g ? tiles_dn : tiles_gu) + size_t(x) * (g ? cap_dn : cap_gu) + size_t(toff[i]) * NT;
-          for (int mm = 0; mm < mu; ++mm)
-            for (int n = 0; n < NT; ++n) tl[mm * NT + n] = make_int2(s, ((m0 + mm) << 8) | n);
+          int4* tl = (g ? tiles_dn : tiles_gu) + size_t(x) * (g ? cap_dn : cap_gu) + size_t(toff[i]) * NT;
+          for (int mm = 0; mm < mu; ++mm) {
+            const int r0 = lo + (m0 + mm) * BM;
+            for (int n = 0; n < NT; ++n) tl[mm * NT + n] = make_int4(s, r0, min(BM, hi - r0), n);
+          }
         }
       }
       if (tid < 8) {
@@ -979,7 +982,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   for (int g = 0; g < 2; ++g) {
     const int NT = g ? nt_dn : nt_gu;
     const int cx = g ? cap_dn : cap_gu;
-    int2* tl = g ? tiles_dn : tiles_gu;
+    int4* tl = g ? tiles_dn : tiles_gu;
     // the host sized the lists for consistent offsets (sum of rows <= T*k); never write past them
     const int total = min(MT * NT, 8 * cx);
     for (int L = tid; L < total; L += kSchedThreads) {
@@ -998,7 +1001,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
         base += (total - x + 7) / 8;
         ++x;
       }
-      tl[size_t(x) * cx + (L - base)] = make_int2(s, (m << 8) | n);
+      const int slo = min(max(off[s], 0), cap), shi = min(max(off[s + 1], slo), cap);
+      const int r0 = slo + m * BM;
+      tl[size_t(x) * cx + (L - base)] = make_int4(s, r0, min(BM, shi - r0), n);
     }
     if (tid < 8) counts[8 * g + tid] = (total - tid + 7) / 8;
   }
@@ -1057,7 +1062,7 @@ static hipError_t gate_up_t(const GemmArgs& g, hipStream_t st) {
     x = g.xb;
   }
   gemm::gemm_kernel<WD, true><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-      static_cast<const uint8_t*>(g.w_gu), g.s_gu, static_cast<const uint16_t*>(x), g.perm, g.off, g.tiles_gu,
+      static_cast<const uint8_t*>(g.w_gu), g.s_gu, static_cast<const uint16_t*>(x), g.perm, g.tiles_gu,
       g.counts, g.S, g.T, g.k, g.H, 2 * g.I, g.I, g.a);
   return hipGetLastError();
 }
@@ -1067,7 +1072,7 @@ static hipError_t down_t(const GemmArgs& g, hipStream_t st) {
   const size_t grid = gemm_tile_slots(g.T, g.k, g.S, gemm_nt_down(g.H));
   if (grid == 0) return hipSuccess;
   gemm::gemm_kernel<WD, false><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-      static_cast<const uint8_t*>(g.w_d), g.s_d, static_cast<const uint16_t*>(g.a), nullptr, g.off, g.tiles_dn,
+      static_cast<const uint8_t*>(g.w_d), g.s_d, static_cast<const uint16_t*>(g.a), nullptr, g.tiles_dn,
       g.counts + 8, g.S, g.T, g.k, g.I, g.H, g.I, g.y);
   return hipGetLastError();
 }
@@ -1077,7 +1082,7 @@ static hipError_t gate_up_q_t(const GemmArgs& g, hipStream_t st) {
   const size_t grid = gemm_tile_slots(g.T, g.k, g.S, gemm_nt_gate_up(g.I));
   if (grid == 0) return hipSuccess;
   gemm::gemm_q_kernel<WD, true><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-      static_cast<const uint8_t*>(g.w_gu), g.s_gu, g.xq, g.xs, g.perm, g.off, g.tiles_gu, g.counts, g.S, g.T,
+      static_cast<const uint8_t*>(g.w_gu), g.s_gu, g.xq, g.xs, g.perm, g.tiles_gu, g.counts, g.S, g.T,
       g.k, g.H, 2 * g.I, g.I, nullptr, g.aq, g.as);
   return hipGetLastError();
 }
@@ -1087,7 +1092,7 @@ static hipError_t down_q_t(const GemmArgs& g, hipStream_t st) {
   const size_t grid = gemm_tile_slots(g.T, g.k, g.S, gemm_nt_down(g.H));
   if (grid == 0) return hipSuccess;
   gemm::gemm_q_kernel<WD, false><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
-      static_cast<const uint8_t*>(g.w_d), g.s_d, g.aq, g.as, nullptr, g.off, g.tiles_dn, g.counts + 8, g.S,
+      static_cast<const uint8_t*>(g.w_d), g.s_d, g.aq, g.as, nullptr, g.tiles_dn, g.counts + 8, g.S,
       g.T, g.k, g.I, g.H, g.I, g.y, nullptr, nullptr);
   return hipGetLastError();
 }

@@ -62,8 +62,8 @@ struct GemmArgs {
   uint8_t* xs;          // [T, H/32]
   uint8_t* aq;          // [T*k, I]
   uint8_t* as;          // [T*k, I/32]
-  int2* tiles_gu;       // tile lists written by the scheduler
-  int2* tiles_dn;
+  int4* tiles_gu;       // tile lists written by the scheduler: {slot, first row, rows, n tile}
+  int4* tiles_dn;
   int32_t* counts;      // [16]: tiles per XCD of the gate/up GEMM, then of the down GEMM
 };
 size_t gemm_tiles_max(int T, int k, int S, int nt);

@@ -148,8 +148,8 @@ struct Carve {
 struct FfnWs {
   void* a;
   void* xb;
-  int2* tiles_gu;
-  int2* tiles_dn;
+  int4* tiles_gu;
+  int4* tiles_dn;
   int32_t* counts;
   uint8_t *xq, *xs, *aq, *as;
   size_t used;
@@ -161,8 +161,8 @@ FfnWs carve_ffn(void* ws, const moe_weights* w, int T, int k, int mode) {
   c.take<char>(256);
   f.a = c.take<char>(R * w->I * sizeof(float));
   f.xb = c.take<char>(size_t(T) * w->H * 2);
-  f.tiles_gu = c.take<int2>(moe::gemm_tile_slots(T, k, w->S, moe::gemm_nt_gate_up(w->I)) * sizeof(int2));
-  f.tiles_dn = c.take<int2>(moe::gemm_tile_slots(T, k, w->S, moe::gemm_nt_down(w->H)) * sizeof(int2));
+  f.tiles_gu = c.take<int4>(moe::gemm_tile_slots(T, k, w->S, moe::gemm_nt_gate_up(w->I)) * sizeof(int4));
+  f.tiles_dn = c.take<int4>(moe::gemm_tile_slots(T, k, w->S, moe::gemm_nt_down(w->H)) * sizeof(int4));
   f.counts = c.take<int32_t>(16 * sizeof(int32_t));
   if (mode == MOE_MODE_B) {
     f.xq = c.take<uint8_t>(size_t(T) * w->H);

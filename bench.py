@@ -58,10 +58,16 @@ def log(*a):
 
 
 def source_hash(paths) -> str:
+    """Hash of the code in `paths` with comments and whitespace removed, so that a recorded
+    counter figure outlives edits of the comments but not of the code."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

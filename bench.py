@@ -518,8 +518,7 @@ def run(args):
     slot_bytes_d = (w.w_d.numel() * w.w_d.element_size() + (0 if w.s_d is None else w.s_d.numel() * w.s_d.element_size())) // S
     xb = 2 if cfg.xdtype == "bf16" else 4
 
-    gemm = path == moe.MOE_PATH_GEMM or (path == moe.MOE_PATH_AUTO and cfg.wdtype != "f32" and H % 64 == 0
-                                         and I % 64 == 0 and T * k > 4 * S)
+    gemm = moe.moe_resolve_path(desc, T, k, path, mode) == moe.MOE_PATH_GEMM
 
     def gate_up_bytes(r):
         touched, n_res, _ = per_rot[r]

@@ -65,8 +65,11 @@ typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scor
 /* Expert-FFN implementation.  GEMV streams each touched slot's weights once per group of rows
  * (any weight dtype).  GEMM runs 128-row tiles on the matrix cores and needs bf16 weights with H
  * and I multiples of 64, or FP8 / MXFP4 weights with H and I multiples of 128 (MXFP4: at most
- * 4096); see moe_mode for mode B.  AUTO picks GEMM when it is available and T*k > 4*S, else
- * GEMV.  Asking for GEMM where it is not available fails with MOE_ERR_UNSUPPORTED.
+ * 4096); see moe_mode for mode B.  AUTO picks GEMM when it is available and T*k exceeds c*S,
+ * else GEMV, with c by weight format from measured crossovers (MI355X, H = 4096, I = 1024):
+ * bf16 2.75, FP8 2, MXFP4 0.5 (the multi-row MXFP4 GEMV decodes every weight per row on the
+ * vector units and loses to the matrix cores from about 0.5 rows per slot).  moe_resolve_path
+ * returns the choice.  Asking for GEMM where it is not available fails with MOE_ERR_UNSUPPORTED.
  * Batch invariance: with a fixed path (GEMV or GEMM, in either mode) a token's output is the
  * same bits whatever batch it is computed in -- every output element is reduced in a fixed
  * order whatever other rows share its slot or tile.  AUTO is not batch-invariant: the two
@@ -312,6 +315,10 @@ const char* moe_status_string(int status);
 const char* moe_last_error(void);
 /* Library version string. */
 const char* moe_version(void);
+/* The implementation moe_expert_ffn / moe_expert_gate_up / moe_expert_down run for these
+ * arguments: `path` itself when it is MOE_PATH_GEMV or MOE_PATH_GEMM, AUTO's choice otherwise
+ * (see moe_path).  Returns MOE_PATH_GEMV or MOE_PATH_GEMM, or -1 for invalid weights or path. */
+int moe_resolve_path(const moe_weights* w, int T, int k, int path, int mode);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,7 @@ _SIGS = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),
+    "moe_resolve_path": (_I, [_W, _I, _I, _I, _I]),
 }
 
 _lib = None
@@ -185,6 +186,10 @@ def moe_route_permute(x, x_dtype, T, H, w_router, logits, bias, cfg, slot_map, S
 
 def moe_expert_ffn_workspace_size(w, T, k, path, mode) -> int:
     return lib().moe_expert_ffn_workspace_size(_ref(w), T, k, path, mode)
+
+
+def moe_resolve_path(w, T, k, path, mode) -> int:
+    return lib().moe_resolve_path(_ref(w), T, k, path, mode)
 
 
 def moe_expert_ffn(w, x, x_dtype, T, k, perm, slot_offsets, path, mode, y_perm, ws, ws_bytes,

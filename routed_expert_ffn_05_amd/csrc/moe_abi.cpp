@@ -110,9 +110,23 @@ bool gemm_capable(const moe_weights* w, int mode) {
 
 // AUTO: the GEMM path once slots hold several rows on average (measured crossover: the GEMV
 // streams weights at the same rate but re-reads them per group of rows)
+// AUTO: the matrix-core path once T*k exceeds c*S, c by weight format (4c below), from the
+// crossovers measured on MI355X at H = 4096, I = 1024: FP8 (S = 384) between T = 88 and 96
+// (T*k ~ 1.85 S), bf16 (S = 384) between T = 112 and 144 (~ 2.6 S), MXFP4 (110 of 384 slots
+// resident) between T = 4 and 8 (~ 0.5 S): the multi-row MXFP4 GEMV decodes each weight per row
+// on the vector units.
+int auto_gemm_threshold4(int wdtype) {
+  switch (wdtype) {
+    case MOE_BF16: return 11;
+    case MOE_FP8_E4M3_B128: return 8;
+    case MOE_MXFP4: return 2;
+  }
+  return 16;
+}
+
 int resolve_path(int path, int T, int k, const moe_weights* w, int mode) {
   if (path != MOE_PATH_AUTO) return path;
-  if (gemm_capable(w, mode) && (long long)T * k > 4LL * w->S) return MOE_PATH_GEMM;
+  if (gemm_capable(w, mode) && 4LL * T * k > (long long)auto_gemm_threshold4(w->wdtype) * w->S) return MOE_PATH_GEMM;
   return MOE_PATH_GEMV;
 }
 
@@ -280,6 +294,12 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, int T, const moe_r
 }
 
 // ---------------------------------------------------------------------------------------------
+int moe_resolve_path(const moe_weights* w, int T, int k, int path, int mode) {
+  if (check_weights(w) != MOE_OK || k < 1 || k > kMaxK || T < 0) return -1;
+  if (check_path_mode(path, mode, w) != MOE_OK) return -1;
+  return resolve_path(path, T, k, w, mode);
+}
+
 size_t moe_expert_ffn_workspace_size(const moe_weights* w, int T, int k, int path, int mode) {
   if (!w || T < 0 || k < 1 || w->I < 1) return 0;
   return ffn_ws_size(w, T, k, resolve_path(path, T, k, w, mode), mode);

@@ -191,3 +191,27 @@ def test_plan_validation(L):
 def test_last_error_is_per_call(L):
     _expect(moe.MOE_ERR_UNSUPPORTED, moe.moe_combine, FAKE, FAKE, FAKE, 4, 2, 30, FAKE, moe.MOE_F32, 0)
     assert "H = 30" in moe.lib().moe_last_error().decode()
+
+
+def test_auto_path_crossovers(L):
+    """AUTO's choice between the GEMV and the matrix cores (host logic, no device work): GEMM once
+    T*k exceeds c*S with c = 2.75 (bf16), 2 (FP8), 0.5 (MXFP4), where the measured crossovers lie;
+    an explicit path passes through; invalid arguments give -1."""
+    def w(dt, S, H=4096, I=1024):
+        return moe.weights(dt, S, H, I, FAKE, FAKE, FAKE, FAKE)
+    A, GEMV, GEMM = moe.MOE_PATH_AUTO, moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM
+    rp = lambda wd, T, k=8, path=A, mode=moe.MOE_MODE_A: moe.moe_resolve_path(wd, T, k, path, mode)
+    bf, f8, f4 = w("bf16", 384), w("fp8", 384), w("mxfp4", 110)
+    # the stated workloads keep their paths: decode on the GEMV, prefill on the matrix cores
+    assert rp(bf, 4) == GEMV and rp(f8, 32) == GEMV and rp(f4, 1) == GEMV
+    assert rp(f8, 4096) == GEMM and rp(f4, 4096) == GEMM
+    # thresholds: bf16 T*k > 1056, FP8 > 768, MXFP4 (S = 110) > 55
+    assert rp(bf, 132) == GEMV and rp(bf, 133) == GEMM
+    assert rp(f8, 96) == GEMV and rp(f8, 97) == GEMM
+    assert rp(f4, 6) == GEMV and rp(f4, 7) == GEMM
+    # an explicit path is returned as is; fp32 weights never take the matrix cores
+    assert rp(f8, 4096, path=GEMV) == GEMV and rp(bf, 1, path=GEMM) == GEMM
+    assert rp(w("f32", 8, 256, 128), 4096) == GEMV
+    # mode B needs FP8 / MXFP4 weights on the matrix-core path: bf16 stays on the GEMV
+    assert rp(bf, 4096, mode=moe.MOE_MODE_B) == GEMV and rp(f8, 4096, mode=moe.MOE_MODE_B) == GEMM
+    assert rp(w("fp8", 384, H=4100), 4) == -1 and rp(f8, 4, path=9) == -1 and rp(f8, 4, k=0) == -1

@@ -690,7 +690,14 @@ def cpu_baseline(cfg, rot, host_w, slot_map, budget_s):
             log(f"cpu oracle batch {batches}: {spent:.1f}s")
         if spent >= budget_s:
             break
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(n_tok / spent, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "cpus_available": len(os.sched_getaffinity(0)),
             "sample": f"{batches} batch(es) x {cfg.T} tokens of the same workload through the whole fp64 "
                       f"oracle layer (routing, permutation, per-slot dequantisation, FFN, combine), "
                       f"{spent:.1f} s"}

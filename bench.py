@@ -605,7 +605,16 @@ def run(args):
         torch.cuda.synchronize()
         log(f"copy probe: {nb} bytes read and written")
 
+    # a record belongs to one workload: every option that changes the bytes a launch moves is part
+    # of its key, so that a variant run finds no record (traffic null) rather than another's
     key = f"{cfg.name}_T{T}"
+    if args.E is not None:
+        key += f"_E{E}"
+    if not gemm and mode == moe.MOE_MODE_B:
+        key += "_modeB"
+    for flag in ("plan_slots", "lru", "tiers"):
+        if getattr(args, flag):
+            key += "_" + flag
     kind = ("gemm_q" if mode == moe.MOE_MODE_B else "gemm") if gemm else "gemv"
     traffic = recorded_traffic(kind, key)
     tflops = sum(gate_up_flops(i % len(rot)) for i in range(args.steps)) / (sum(gu_ms) / 1e3) / 1e12

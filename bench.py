@@ -630,6 +630,9 @@ def run(args):
         tgbs = traffic / (float(np.mean(gu_ms)) / 1e3) / 1e9
         roofline["traffic_GBs"] = round(tgbs, 1)
         roofline["traffic_vs_algorithmic"] = round(traffic / (sum(gu_bytes) / len(gu_bytes)), 3)
+        # the counter rate and the event rate should agree within 10 %; a disagreement flags re-reads
+        # (or a record that no longer describes the launch)
+        roofline["traffic_agrees"] = bool(abs(tgbs / achieved - 1.0) <= 0.10)
     if gemm:
         # mode A runs bf16 MFMA on decoded weights; mode B the block-scaled f8f6f4 MFMA with E4M3
         # activations, which issues at the FP8 rate whether the weights are E4M3 or E2M1

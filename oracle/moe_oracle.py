@@ -363,19 +363,31 @@ def e4m3fn_round(v: np.ndarray) -> np.ndarray:
     return np.sign(v) * np.minimum(r, 448.0)
 
 
-def act_quant_mx_e4m3(a: np.ndarray, block: int = 32) -> np.ndarray:
-    """Per row, per ``block`` consecutive elements: X = floor(log2 amax) - 8 (e4m3's largest
-    exponent), elements e4m3fn(v / 2^X) saturated at +-448, then scaled back by 2^X.  An
-    all-zero block stays zero."""
+def act_quant_mx_e4m3_parts(a: np.ndarray, block: int = 32):
+    """The two parts of the OCP MX quantisation with E4M3 elements, per row and per ``block``
+    consecutive elements: the shared scale exponent X and the element values q (e4m3fn values,
+    fp64), so that the quantised activation is q * 2^X.
+
+    X = floor(log2 amax) - 8 (8 is e4m3's largest exponent), kept inside the E8M0 scale range
+    [-127, 127] (OCP MX v1.0: E8M0 encodes 2^-127 .. 2^127; finite amax keeps X <= 119, so only
+    the lower end binds, for blocks with amax < 2^-118); an all-zero block has X = 0.  Each
+    element is e4m3fn(v / 2^X), nearest even, saturated at +-448."""
     a = np.asarray(a, np.float64)
     n, K = a.shape
     assert K % block == 0
     b = a.reshape(n, K // block, block)
     amax = np.abs(b).max(axis=2)
     _, ex = np.frexp(amax)
-    X = np.where(amax > 0, ex - 1 - 8, 0)
+    X = np.where(amax > 0, np.maximum(ex - 1 - 8, -127), 0)
     q = e4m3fn_round(np.ldexp(b, -X[:, :, None]))
-    return np.ldexp(q, X[:, :, None]).reshape(n, K)
+    return X.astype(np.int64), q.reshape(n, K)
+
+
+def act_quant_mx_e4m3(a: np.ndarray, block: int = 32) -> np.ndarray:
+    """The quantised activation q * 2^X (fp64) of ``act_quant_mx_e4m3_parts``."""
+    X, q = act_quant_mx_e4m3_parts(a, block)
+    n, K = q.shape
+    return np.ldexp(q.reshape(n, K // block, block), X[:, :, None]).reshape(n, K)
 
 
 # ----------------------------------------------------------------------------------------------

@@ -140,6 +140,33 @@ def test_act_quant_block_rule():
     assert np.all(q[0, 3:32] == 0) and np.all(q[0, 34:] == 0)
 
 
+def test_act_quant_e8m0_lower_clamp():
+    # OCP MX v1.0: the E8M0 scale encodes 2^-127 .. 2^127, so X never drops below -127.  A block
+    # with amax = 2^-121 would want X = -129; clamped it takes X = -127 (scale byte 0), and its
+    # elements are coded against 2^-127: 2^-121 -> 2^6, 3 * 2^-126 -> 6, 5 * 2^-136 -> 5 * 2^-9
+    # (an exact e4m3 subnormal), and 2^-140 -> 2^-13, below half the smallest e4m3 subnormal
+    # (2^-9), so 0.  A block with amax = 2^-118 needs no clamp (X = -126).
+    a = np.zeros((1, 96))
+    a[0, 0] = 2.0 ** -121
+    a[0, 1] = 3.0 * 2.0 ** -126
+    a[0, 2] = 2.0 ** -140
+    a[0, 3] = 5.0 * 2.0 ** -136
+    a[0, 32] = 2.0 ** -118                              # X = -126: inside the range
+    a[0, 64] = 1.5 * 2.0 ** -119                        # X = floor(-118.4) - 8 = -127 exactly
+    X, q = O.act_quant_mx_e4m3_parts(a)
+    assert X.tolist() == [[-127, -126, -127]]
+    assert q[0, 0] == 64.0 and q[0, 1] == 6.0 and q[0, 2] == 0.0 and q[0, 3] == 5.0 * 2.0 ** -9
+    assert q[0, 32] == 256.0 and q[0, 64] == 384.0
+    deq = O.act_quant_mx_e4m3(a)
+    assert deq[0, 0] == a[0, 0] and deq[0, 1] == a[0, 1] and deq[0, 2] == 0.0 and deq[0, 3] == a[0, 3]
+    # a subnormal-range element that the clamp does change: 2^-138 -> 2^-11 against 2^-127 (rounds
+    # to 0); against 2^-129 it would be 2^-9, the smallest e4m3 subnormal
+    b = np.zeros((1, 32))
+    b[0, 0] = 2.0 ** -121
+    b[0, 1] = 2.0 ** -138
+    assert O.act_quant_mx_e4m3(b)[0, 1] == 0.0
+
+
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp4"])
 def test_generator_encoders_roundtrip(wdtype):
     # the generator's encoders (input production) decoded by the oracle stay close to the

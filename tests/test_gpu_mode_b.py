@@ -23,8 +23,8 @@ GEMM_SCALE_TOL = 8e-2
 CASES = {
     # K = 256 / 128: scale rows of 8 / 4 bytes (copied, not rotated), ragged groups
     "fp8_zipf": gen.config("prefill_fp8_zipf", T=300, H=256, E=32, I=128, k=8),
-    # up rows straddling 128-row FP8 scale blocks, K = 384 / 320
-    "fp8_big_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=8, I=320, k=2),
+    # ragged last N tiles in both projections (I = H = 384), K = 384: E8M0 rows of 12 bytes
+    "fp8_big_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=8, I=384, k=2),
     # K = 1024 / 512: rotated scale rows loaded by direct loads; compact map with misses
     "mxfp4_compact": gen.config("compact_mxfp4", T=256, H=1024, E=16, I=512, k=4, resident=11),
     "mxfp4_ragged": gen.config("compact_mxfp4", T=200, H=512, E=24, I=192, k=6, resident=9),
@@ -79,6 +79,10 @@ def test_quantizer_bit_exact():
     x[11, :32] = 1.0
     x[11, 0] = 511.0  # amax 511 -> X = 0; 448 < 480 < 511 saturate
     x[11, 1] = 480.0
+    # a block whose amax (2^-121) wants X = -129: the E8M0 range keeps X = -127 (scale byte 0);
+    # its elements stay normal fp32 numbers, and the scale byte is compared directly below
+    x[13, 64:96] = 2.0 ** -121 * (1.0 + np.arange(32) / 32.0) / 2.0
+    x[13, 64] = 2.0 ** -121
     for dt in ("f32", "bf16"):
         _banner(f"quantizer {dt}")
         if dt == "f32":
@@ -92,6 +96,8 @@ def test_quantizer_bit_exact():
             d_x = D.to_device(bits)
             xdt = moe.MOE_BF16
         ref = O.act_quant_mx_e4m3(x64)
+        ref_X, _ = O.act_quant_mx_e4m3_parts(x64)
+        assert ref_X[13, 2] == -127
         codes = torch.empty((rows, K), dtype=torch.uint8, device="cuda")
         scales = torch.empty((rows, K // 32), dtype=torch.uint8, device="cuda")
         deq = torch.empty((rows, K), dtype=torch.float32, device="cuda")
@@ -105,6 +111,7 @@ def test_quantizer_bit_exact():
         assert np.array_equal(dqb, ref)
         c = codes.cpu().numpy()
         s = scales.cpu().numpy().astype(np.int64) - 127
+        assert np.array_equal(s, ref_X), "E8M0 scale bytes"
         val = O.e4m3fn_to_f64(c) * np.exp2(np.repeat(s, 32, axis=1))
         assert np.array_equal(val, ref)
 
@@ -139,6 +146,7 @@ def test_mode_b_layer(case):
     res = g.layer(mode=moe.MOE_MODE_B)
     flipped = check_routing(res["topk_idx"], res["topk_w"], ref)
     keep = np.array([t not in flipped for t in range(inp.cfg.T)], bool)
-    gemm = _gemm_ok(inp.cfg) and inp.cfg.T * inp.cfg.k > 4 * inp.cfg.S  # the path AUTO takes
+    # the path AUTO takes, as the library resolves it
+    gemm = moe.moe_resolve_path(g.w.desc, inp.cfg.T, inp.cfg.k, moe.MOE_PATH_AUTO, moe.MOE_MODE_B) == moe.MOE_PATH_GEMM
     assert_fp_close(res["out"][keep], ref["out"][keep], f"{name} layer out (mode B)",
                     scale_tol=GEMM_SCALE_TOL if gemm else 2e-2)

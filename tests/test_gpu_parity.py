@@ -20,11 +20,13 @@ SMALL = {
     "fp8_zipf": gen.config("prefill_fp8_zipf", T=300, H=256, E=32, I=128, k=8),
     "mxfp4_compact": gen.config("compact_mxfp4", T=53, H=512, E=40, I=160, k=6, resident=13),
     "mxfp4_compact_t1": gen.config("compact_mxfp4", T=1, H=256, E=16, I=128, k=4, resident=5),
-    # shapes for the matrix-core path (H, I multiples of 64): several M tiles per slot, FP8 up rows
-    # straddling 128-row scale blocks (I % 128 == 64), ragged 32-row blocks
+    # shapes for the matrix-core path: bf16 weights (H, I multiples of 64) with several M tiles per
+    # slot and ragged 32-row blocks; FP8 with a ragged last N tile in both projections (I = 384:
+    # three 128-column gate/up tiles; H = 384: a 256- and a 128-column down tile); MXFP4 with 20
+    # E8M0 scales per gate/up row (H = 640, copied rather than loaded rotated) and a compact map
     "bf16_gemm": gen.config("decode_bf16", T=70, H=512, E=12, I=192, k=4),
-    "fp8_big_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=8, I=320, k=2),
-    "mxfp4_gemm_compact": gen.config("compact_mxfp4", T=200, H=512, E=24, I=192, k=6, resident=9),
+    "fp8_big_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=8, I=384, k=2),
+    "mxfp4_gemm_compact": gen.config("compact_mxfp4", T=200, H=640, E=24, I=384, k=6, resident=9),
     # the matrix-core path with FP8 / MXFP4 weights (K multiples of 128): several M tiles per slot
     "fp8_gemm_groups": gen.config("prefill_fp8_zipf", T=400, H=384, E=4, I=256, k=2),
     "mxfp4_gemm_groups": gen.config("compact_mxfp4", T=300, H=512, E=12, I=256, k=4, resident=5),

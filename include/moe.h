@@ -68,17 +68,28 @@ typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scor
  * 4096); see moe_mode for mode B.  AUTO picks GEMM when it is available and T*k exceeds c*S,
  * else GEMV, with c by weight format from measured crossovers (MI355X, H = 4096, I = 1024):
  * bf16 2.75, FP8 2, MXFP4 0.5 (the multi-row MXFP4 GEMV decodes every weight per row on the
- * vector units and loses to the matrix cores from about 0.5 rows per slot).  moe_resolve_path
- * returns the choice.  Asking for GEMM where it is not available fails with MOE_ERR_UNSUPPORTED.
- * Batch invariance: with a fixed path (GEMV or GEMM, in either mode) a token's output is the
- * same bits whatever batch it is computed in -- every output element is reduced in a fixed
- * order whatever other rows share its slot or tile.  AUTO is not batch-invariant: the two
- * paths round differently (the GEMM path keeps a = silu(g)*u in bf16, the GEMV path in fp32).
+ * vector units and loses to the matrix cores from about 0.5 rows per slot).  INVARIANT picks
+ * GEMM whenever it is available for the weights and mode, else GEMV, whatever T is.
+ * moe_resolve_path returns the choice.  Asking for GEMM where it is not available fails with
+ * MOE_ERR_UNSUPPORTED.
+ * Batch invariance (vLLM-Moet README, RTX PRO 6000 table, row "quality": identical requests give
+ * identical results at any batch size): with GEMV, GEMM or INVARIANT a token's output is the
+ * same bits whatever batch it is computed in -- each path reduces every output element in a
+ * fixed order whatever other rows share its slot or tile, and INVARIANT's choice depends on the
+ * weights and mode only.  AUTO is not batch-invariant: its choice depends on T, and the two paths
+ * round differently (the GEMM path keeps a = silu(g)*u in bf16, the GEMV path in fp32).
  * GEMM tile order: the tiles are dealt to the GPU's eight XCDs in cost-sorted units of a slot's
- * M tiles; the environment variable MOE_GEMM_TILE_ORDER=contiguous (read at every call) selects
- * the plain (slot, M tile, N tile) order in eight contiguous runs instead.  The order changes
- * only which compute unit runs a tile, never the arithmetic: both give the same bits. */
-typedef enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 } moe_path;
+ * M tiles.  MOE_PATH_TILES_CONTIGUOUS, or'ed into any path value, deals them in the plain
+ * (slot, M tile, N tile) order in eight contiguous runs instead (the order the scheduler falls
+ * back to when its tables outgrow its LDS).  The order changes only which compute unit runs a
+ * tile, never the arithmetic: both give the same bits. */
+typedef enum moe_path {
+  MOE_PATH_AUTO = 0,
+  MOE_PATH_GEMV = 1,
+  MOE_PATH_GEMM = 2,
+  MOE_PATH_INVARIANT = 3,
+  MOE_PATH_TILES_CONTIGUOUS = 0x100 /* flag, or'ed into one of the above */
+} moe_path;
 
 /* Expert-FFN arithmetic.  MODE_A: activations kept in bf16/fp32, weights decoded exactly,
  * fp32 accumulation.  MODE_B: the activations entering each projection (x before gate/up, a

@@ -20,7 +20,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_FP8_E4M3_B128, MOE_MXFP4 = range(4)
 # moe_score / moe_path / moe_mode
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM, MOE_PATH_INVARIANT = 0, 1, 2, 3
+MOE_PATH_TILES_CONTIGUOUS = 0x100  # flag, or'ed into a path value
 MOE_MODE_A, MOE_MODE_B = 0, 1
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3_B128, "mxfp4": MOE_MXFP4}

@@ -124,15 +124,20 @@ int auto_gemm_threshold4(int wdtype) {
   return 16;
 }
 
+// the implementation a path value asks for (its flag bits removed): GEMV or GEMM
 int resolve_path(int path, int T, int k, const moe_weights* w, int mode) {
+  path &= ~MOE_PATH_TILES_CONTIGUOUS;
+  if (path == MOE_PATH_INVARIANT) return gemm_capable(w, mode) ? MOE_PATH_GEMM : MOE_PATH_GEMV;
   if (path != MOE_PATH_AUTO) return path;
   if (gemm_capable(w, mode) && 4LL * T * k > (long long)auto_gemm_threshold4(w->wdtype) * w->S) return MOE_PATH_GEMM;
   return MOE_PATH_GEMV;
 }
 
 int check_path_mode(int path, int mode, const moe_weights* w) {
-  if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_GEMM)
+  const int base = path & ~MOE_PATH_TILES_CONTIGUOUS;
+  if (base != MOE_PATH_AUTO && base != MOE_PATH_GEMV && base != MOE_PATH_GEMM && base != MOE_PATH_INVARIANT)
     return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
+  path = base;
   if (mode != MOE_MODE_A && mode != MOE_MODE_B) return fail(MOE_ERR_INVALID_ARG, "unknown mode %d", mode);
   if (mode == MOE_MODE_B && (w->H % 32 || w->I % 32))
     return fail(MOE_ERR_UNSUPPORTED, "mode B needs H and I multiples of 32 (one E8M0 scale per 32 elements)");
@@ -346,9 +351,11 @@ moe::GemvArgs gemv_args(const moe_weights* w, const void* x, int x_dtype, int T,
 }
 
 moe::GemmArgs gemm_args(const moe_weights* w, const void* x, int x_dtype, int T, int k,
-                        const int32_t* perm, const int32_t* off, float* y, void* ws, int mode) {
+                        const int32_t* perm, const int32_t* off, float* y, void* ws, int mode,
+                        int path = 0) {
   const FfnWs f = carve_ffn(ws, w, T, k, mode);
   moe::GemmArgs g{};
+  g.tiles_contiguous = (path & MOE_PATH_TILES_CONTIGUOUS) != 0;
   g.wdt = w->wdtype;
   g.xdt = x_dtype;
   g.S = w->S;
@@ -390,7 +397,7 @@ int moe_expert_gate_up(const moe_weights* w, const void* x, int x_dtype, int T, 
   const int rp = resolve_path(path, T, k, w, mode);
   const int R = T * k;
   if (rp == MOE_PATH_GEMM) {
-    moe::GemmArgs g = gemm_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws, mode);
+    moe::GemmArgs g = gemm_args(w, x, x_dtype, T, k, perm, slot_offsets, nullptr, ws, mode, path);
     hipError_t e = hipSuccess;
     if (mode == MOE_MODE_B)  // E4M3 codes + E8M0 scales of x
       e = moe::launch_act_quant(x, x_dtype, T, w->H, nullptr, g.xq, g.xs, nullptr, 0, st);
@@ -610,8 +617,8 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
                             miss_token, miss_expert, miss_weight, L.rp, L.rp_bytes, stream));
   if (T == 0) return MOE_OK;
   const size_t ffn_bytes = ffn_ws_size(w, T, cfg->k, rp, mode);
-  MOE_TRY(moe_expert_ffn(w, x, x_dtype, T, cfg->k, L.perm, L.offsets, rp, mode, L.y, L.ffn,
-                         ffn_bytes, stream));
+  MOE_TRY(moe_expert_ffn(w, x, x_dtype, T, cfg->k, L.perm, L.offsets, rp | (path & MOE_PATH_TILES_CONTIGUOUS), mode,
+                         L.y, L.ffn, ffn_bytes, stream));
   return moe_combine(L.y, L.inv, tw, T, cfg->k, w->H, out, out_dtype, stream);
 }
 

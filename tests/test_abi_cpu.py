@@ -215,3 +215,23 @@ def test_auto_path_crossovers(L):
     # mode B needs FP8 / MXFP4 weights on the matrix-core path: bf16 stays on the GEMV
     assert rp(bf, 4096, mode=moe.MOE_MODE_B) == GEMV and rp(f8, 4096, mode=moe.MOE_MODE_B) == GEMM
     assert rp(w("fp8", 384, H=4100), 4) == -1 and rp(f8, 4, path=9) == -1 and rp(f8, 4, k=0) == -1
+
+
+def test_invariant_path_and_tile_order_flag(L):
+    """INVARIANT resolves by the weights and mode alone -- the matrix cores wherever they take the
+    shape, else the GEMV -- so its choice never depends on T; the tile-order flag is accepted on
+    every path and leaves the choice alone; other flag bits are rejected."""
+    def w(dt, S, H=4096, I=1024):
+        return moe.weights(dt, S, H, I, FAKE, FAKE, FAKE, FAKE)
+    INV, GEMV, GEMM = moe.MOE_PATH_INVARIANT, moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM
+    C = moe.MOE_PATH_TILES_CONTIGUOUS
+    rp = lambda wd, T, path, mode=moe.MOE_MODE_A: moe.moe_resolve_path(wd, T, 8, path, mode)
+    for wd in (w("bf16", 384), w("fp8", 384), w("mxfp4", 110)):
+        assert {rp(wd, T, INV) for T in (1, 4, 32, 4096)} == {GEMM}
+        assert rp(wd, 1, GEMV | C) == GEMV and rp(wd, 1, GEMM | C) == GEMM and rp(wd, 4096, moe.MOE_PATH_AUTO | C) == GEMM
+    # shapes the matrix cores do not take stay on the GEMV for every T
+    for wd in (w("f32", 8, 256, 128), w("fp8", 384, H=4096, I=1056), w("bf16", 384, H=4096, I=1000)):
+        assert {rp(wd, T, INV) for T in (1, 4096)} == {GEMV}
+    assert rp(w("bf16", 384), 4096, INV, mode=moe.MOE_MODE_B) == GEMV
+    assert rp(w("fp8", 384), 1, INV, mode=moe.MOE_MODE_B) == GEMM
+    assert rp(w("fp8", 384), 4, 0x200 | GEMM) == -1 and rp(w("fp8", 384), 4, C | 7) == -1

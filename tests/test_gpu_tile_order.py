@@ -1,10 +1,10 @@
 """GPU: the GEMM path's tile order across the XCDs changes placement only.  The scheduler deals
 (slot, M tile, N tile) tiles to the eight XCDs in cost-sorted units (the default) or, as its
-fallback, in eight contiguous runs of the plain order (MOE_GEMM_TILE_ORDER=contiguous).  Every
+fallback, in eight contiguous runs of the plain order (MOE_PATH_TILES_CONTIGUOUS or'ed into the
+path).  Every
 output element is computed by one tile in a fixed reduction order, so both orders must give the
 same bits, on skewed routing (a few hot slots of many M tiles), on few slots, and on uniform
 routing, for both projections (y) in modes A and B."""
-import os
 import sys
 
 import numpy as np
@@ -41,12 +41,8 @@ def test_tile_orders_give_identical_bits(case, mode):
     for order in ("balanced", "contiguous"):
         print(f"[gpu-tile-order] case={case} mode={mode} order={order} T={cfg.T} E={cfg.E} S={cfg.S}", flush=True)
         sys.stdout.flush()
-        if order == "contiguous":
-            os.environ["MOE_GEMM_TILE_ORDER"] = "contiguous"
-        try:
-            ys[order] = g.expert_ffn(rp["perm"], rp["slot_offsets"], path=moe.MOE_PATH_GEMM, mode=m)
-        finally:
-            os.environ.pop("MOE_GEMM_TILE_ORDER", None)
+        path = moe.MOE_PATH_GEMM | (moe.MOE_PATH_TILES_CONTIGUOUS if order == "contiguous" else 0)
+        ys[order] = g.expert_ffn(rp["perm"], rp["slot_offsets"], path=path, mode=m)
     a, b = ys["balanced"], ys["contiguous"]
     assert a.shape == b.shape and a.shape[0] == len(rp["perm"])
     assert np.all(np.isfinite(a)), "rows left unwritten (NaN fill) in the balanced order"

@@ -58,6 +58,13 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu on the hardware exp2 and reciprocal (each about 1 ulp): z * 1 / (1 + 2^(-z log2 e)); the
+// matrix-core epilogues round the result to bf16 (or quantise it), far coarser than the
+// difference from silu() above.  Limits: z -> -inf gives -0 (2^+inf = inf, 1/inf = 0),
+// z -> +inf gives z.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
 
 // Mode B activation quantisation (OCP MX rule with E4M3 elements), shared by the quantisation
 // kernel and the gate/up GEMM's epilogue so both give the same bits.

@@ -32,8 +32,6 @@
 // read from L2 by all N tiles, each weight slice by the M tiles in flight.  Units go out largest
 // first and serpentine over the XCDs, which evens out their work on skewed routing (see
 // schedule_kernel).
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "common.h"
@@ -103,6 +101,43 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int WD>
 __host__ __device__ constexpr size_t row_bytes(int K) {
   return WD == DT_BF16 ? size_t(K) * 2 : WD == DT_FP8 ? size_t(K) : size_t(K) / 2;
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Down epilogue: the tile's y (rows x 256 columns, fp32; accumulator r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4 of its row block, column 32*wave + l%32) leaves through LDS in
+// 16-byte pieces, 64 rows at a time (row stride 264 floats: the two lane halves, 4 rows apart,
+// write disjoint bank halves).  y is read once, by the combine, long after: the stores are
+// non-temporal.  Needs N % 4 == 0 and 64 * 264 * 4 bytes of `lds`; every wave's stage reads and
+// direct loads must be done (the caller waited for its loads).
+template <int NS, typename Acc>
+__device__ __forceinline__ void store_y_tile(const Acc& acc, uint8_t* lds, float* __restrict__ y, int m0, int rows,
+                                             int n0, int N) {
+  constexpr int YS = 264;
+  float* yt = reinterpret_cast<float*>(lds);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ln = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < (NS + 1) / 2; ++half) {
+    __syncthreads();  // the stages (first half) or the previous half's rows are no longer read
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh) {
+      const int ms = 2 * half + mh;
+      if (ms < NS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yt[(mh * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * YS + 32 * wv + ln] = acc[ms][r];
+      }
+    }
+    __syncthreads();
+    const int rh = min(64, rows - 64 * half);  // rows of this half
+    for (int t = tid; t < rh * 64; t += kThreads) {
+      const int m = t >> 6, h = n0 + (t & 63) * 4;
+      if (h < N) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(yt + m * YS + (t & 63) * 4);
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(y + size_t(m0 + 64 * half + m) * N + h));
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -277,11 +312,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
           if (q == j - na) dma16(bsrc[q] + size_t(kk) * (F::ROW), st + AB + (F::INSTR * wv + q) * 1024);
       }
     };
-    // the step's loads are spread over its K sub-steps: group g issues loads [lo(g), lo(g+1))
+    // the step's loads are spread over the first half of its K sub-steps (KG of them), so that
+    // they have the second half to land: group g issues loads [lo(g), lo(g+1))
+    constexpr int KG = KS >= 4 ? KS / 2 : KS;
     auto issue_group = [&](int g, int kk, uint32_t st) {
+      if (g >= KG) return;
 #pragma unroll
       for (int j = 0; j < A_HI + F::INSTR; ++j)
-        if (j < nl && j >= (nl * g) / KS && j < (nl * (g + 1)) / KS) issue_one(j, kk, st);
+        if (j < nl && j >= (nl * g) / KG && j < (nl * (g + 1)) / KG) issue_one(j, kk, st);
     };
 
     f32x16_t acc[NS], tmp[NS];
@@ -361,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 #pragma unroll
     for (int p = 0; p < NST - 1; ++p)
 #pragma unroll
-      for (int g = 0; g < KS; ++g) issue_group(g, min(p, nk - 1), lds0 + p * SB);
+      for (int g = 0; g < KG; ++g) issue_group(g, min(p, nk - 1), lds0 + p * SB);
     int sr = 0;             // stage of step kk
     int sw = NST - 1;       // stage that step kk loads into
     for (int kk = 0; kk < nk; ++kk) {
@@ -418,11 +456,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 #pragma unroll
       for (int ms = 0; ms < NS; ++ms) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-          const float v = acc[ms][r];
-          const float o = __shfl_xor(v, 16);
-          if (ln < 16 && m < rows) at[m * 128 + 16 * wv + ln] = rowok[m] ? f32_to_bf16(silu(v) * o) : uint16_t(0);
+        for (int r = 0; r < 16; r += 2) {
+          // registers r, r+1 are rows m, m+1; lane ln < 16 holds gate values, lane ln + 16 the up
+          // values of the same columns.  One exchange gives the low lane (gate, up) of row m and
+          // the high lane those of row m+1, so each lane forms one silu(g)*u per register pair.
+          const bool lo = ln < 16;
+          const float x0 = acc[ms][r], x1 = acc[ms][r + 1];
+          const float recv = __shfl_xor(lo ? x1 : x0, 16);
+          const float g = lo ? x0 : recv, u = lo ? recv : x1;
+          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3) + (lo ? 0 : 1);
+          if (m < rows) at[m * 128 + 16 * wv + (ln & 15)] = rowok[m] ? f32_to_bf16(silu_fast(g) * u) : uint16_t(0);
         }
       }
       __syncthreads();
@@ -434,18 +477,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
               *reinterpret_cast<const uint4*>(at + m * 128 + c8);
       }
     } else {
-#pragma unroll
-      for (int ms = 0; ms < NS; ++ms) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-          const int h = n0 + 32 * wv + ln;
-          // y is read once, by the combine, long after: streamed past the caches (down GEMM 5 %
-          // faster at the prefill shapes than with cached stores)
-          if (m < rows && h < N)
-            __builtin_nontemporal_store(acc[ms][r], static_cast<float*>(out) + size_t(m0 + m) * N + h);
-        }
-      }
+      store_y_tile<NS>(acc, smem, static_cast<float*>(out), m0, rows, n0, N);
     }
   };
   switch (nsub) {
@@ -741,11 +773,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
 #pragma unroll
       for (int ms = 0; ms < NS; ++ms) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-          const float v = acc[ms][r];
-          const float o = __shfl_xor(v, 16);
-          if (ln < 16 && m < rows) at[m * 128 + 16 * wv + ln] = rowok[m] ? silu(v) * o : 0.0f;
+        for (int r = 0; r < 16; r += 2) {
+          // one silu(g)*u per lane and register pair, as in mode A
+          const bool lo = ln < 16;
+          const float x0 = acc[ms][r], x1 = acc[ms][r + 1];
+          const float recv = __shfl_xor(lo ? x1 : x0, 16);
+          const float g = lo ? x0 : recv, u = lo ? recv : x1;
+          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3) + (lo ? 0 : 1);
+          if (m < rows) at[m * 128 + 16 * wv + (ln & 15)] = rowok[m] ? silu_fast(g) * u : 0.0f;
         }
       }
       __syncthreads();
@@ -774,16 +809,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
         if (part == 0) as_out[size_t(m0 + m) * KB + (n0 >> 5) + blk] = uint8_t(X + 127);
       }
     } else {
-#pragma unroll
-      for (int ms = 0; ms < NS; ++ms) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-          const float v = acc[ms][r];
-          const int h = n0 + 32 * wv + ln;
-          if (m < rows && h < N) __builtin_nontemporal_store(v, out + size_t(m0 + m) * N + h);  // as in mode A
-        }
-      }
+      store_y_tile<NS>(acc, smem, out, m0, rows, n0, N);
     }
   };
   switch (nsub) {
@@ -931,10 +957,19 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
     __syncthreads();
     if (wid < 8) {  // wave x: the units of XCD x (sorted positions 8j + x, or 8j + 7 - x for odd j)
       const int x = wid;
+      // XCD x holds J units j = 0 .. J-1 (largest first); its list takes them from the larger and
+      // the smaller half in turn (even XCDs start with the larger, odd ones with the smaller), so
+      // that matrix-bound and HBM-bound units run side by side and the list ends on a small one
+      const int jl = U >> 3;
+      const int J = jl + (8 * jl + ((jl & 1) ? 7 - x : x) < U ? 1 : 0);
+      const int JH = (J + 1) >> 1, JC = J >> 1;
       int carry = 0;
-      for (int j0 = 0; 8 * j0 < U; j0 += 64) {
-        const int j = j0 + lane;
-        const int i = 8 * j + ((j & 1) ? 7 - x : x);
+      for (int p0 = 0; p0 < J; p0 += 64) {
+        const int p = p0 + lane;
+        int j;
+        if ((x & 1) == 0) j = (p & 1) ? JH + (p >> 1) : (p >> 1);
+        else j = (p & 1) ? (p >> 1) : ((p >> 1) < JC ? JH + (p >> 1) : (p >> 1));
+        const int i = p < J ? 8 * j + ((j & 1) ? 7 - x : x) : U;
         int m = 0;
         if (i < U) {
           const int q = useq[i], s = q & 1023, ui = q >> 10;
@@ -1037,10 +1072,8 @@ hipError_t launch_gemm_schedule(const GemmArgs& g, hipStream_t st) {
   constexpr size_t kDynLdsMax = 150 * 1024;
   const size_t base = sizeof(int32_t) * size_t(g.S + 1);
   const size_t umax = gemm_tiles_max(g.T, g.k, g.S, 1);
-  // MOE_GEMM_TILE_ORDER=contiguous asks for the fallback order (same results, other placement)
-  const char* order = std::getenv("MOE_GEMM_TILE_ORDER");
-  const bool contiguous = order && std::strcmp(order, "contiguous") == 0;
-  const bool fits = !contiguous && base + 2 * sizeof(int32_t) * umax <= kDynLdsMax;
+  // the caller may ask for the fallback order (same results, other placement)
+  const bool fits = !g.tiles_contiguous && base + 2 * sizeof(int32_t) * umax <= kDynLdsMax;
   const size_t lds = fits ? base + 2 * sizeof(int32_t) * umax : base;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm::schedule_kernel,

@@ -38,6 +38,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -417,7 +419,23 @@ def run(args):
     odt = moe.MOE_BF16 if cfg.out_dtype == "bf16" else moe.MOE_F32
     rcfg = moe.routing(E, k, cfg.score, cfg.renorm)
     desc = w.desc
-    path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[args.path]
+    # weight copies: consecutive steps run on different device copies of the same weights, so that
+    # more than 1 GB of distinct weight bytes passes between two uses of one copy (the 256 MB
+    # Infinity Cache cannot serve a step from the previous one); the LRU and two-tier modes
+    # change or pair the weights and keep one copy
+    wbytes = w.nbytes_per_slot * S
+    ncopy = args.weight_copies
+    if ncopy <= 0:
+        ncopy = 1 if wbytes >= 8e9 else max(2, -(-int(1.5e9) // max(wbytes, 1)))
+    if args.lru or args.tiers or args.graph_layers:
+        ncopy = 1
+    ncopy = max(1, min(ncopy, int(48e9 // max(wbytes, 1))))
+    wcopies = [w] + [D.DeviceWeights(w.wdtype, S, H, I, *[t.clone() if t is not None else None
+                                                          for t in (w.w_gu, w.s_gu, w.w_d, w.s_d)])
+                     for _ in range(ncopy - 1)]
+    descs = [c.desc for c in wcopies]
+    path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM,
+            "invariant": moe.MOE_PATH_INVARIANT}[args.path]
     mode = {"A": moe.MOE_MODE_A, "B": moe.MOE_MODE_B}[args.mode]
     R = T * k
     dev = "cuda"
@@ -477,7 +495,7 @@ def run(args):
     def step(i, ev=None, dsc=None, sp=sp):
         # with the LRU every call takes the next batch of the stream, so that no batch comes back
         r = (lru_step[0] if lru else i) % len(rot)
-        dsc = desc if dsc is None else dsc
+        dsc = descs[i % ncopy] if dsc is None else dsc
         moe.moe_route_permute(d_x[r], xdt, T, H, d_wr, d_lg[r], None, rcfg, d_sm, S, topk_idx, topk_w, counts,
                               off, perm, inv, mc if compact else None, mt if compact else None,
                               me if compact else None, mw if compact else None, pws, rp_bytes, sp)
@@ -537,28 +555,40 @@ def run(args):
         step(i)
     torch.cuda.synchronize()
     hip = _hip_runtime()
-    evs = [(TimingEvent(hip), TimingEvent(hip)) for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    end.record(stream)
-    host = time.perf_counter() - wall0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    gu_ms = [a.elapsed_time(b) for a, b in evs]
+    # the timed region: `repeats` blocks of K = args.steps steps each, every block bracketed by a
+    # device synchronisation and its own pair of events; the reported step time is the median
+    # block's.  Step i of the run uses rotation i and weight copy i in turn.
+    R = max(1, args.repeats)
+    evs = [[(TimingEvent(hip), TimingEvent(hip)) for _ in range(args.steps)] for _ in range(R)]
+    block_ms, hosts, walls = [], [], []
+    for rr in range(R):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            step(args.warmup + rr * args.steps + i, evs[rr][i])
+        end.record(stream)
+        hosts.append(time.perf_counter() - wall0)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - wall0)
+        block_ms.append(start.elapsed_time(end))
+    med = int(np.argsort(block_ms)[len(block_ms) // 2])
+    total_ms = block_ms[med]
+    host, wall = hosts[med], walls[med]
+    gu_ms = [a.elapsed_time(b) for blk in evs for a, b in blk]
+    step_ids = [args.warmup + rr * args.steps + i for rr in range(R) for i in range(args.steps)]
     ms_per_step = total_ms / args.steps
     tokens_per_s = T * args.steps / (total_ms / 1e3)
-    gu_bytes = [gate_up_bytes(i % len(rot)) for i in range(args.steps)]
+    gu_bytes = [gate_up_bytes(i % len(rot)) for i in step_ids]
     achieved = sum(gu_bytes) / (sum(gu_ms) / 1e3) / 1e9
-    layer_gbs = sum(layer_bytes(i % len(rot)) for i in range(args.steps)) / (total_ms / 1e3) / 1e9
-    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host enqueue {host * 1e6 / args.steps:.1f} us/step, "
+    med_ids = [args.warmup + med * args.steps + i for i in range(args.steps)]
+    layer_gbs = sum(layer_bytes(i % len(rot)) for i in med_ids) / (total_ms / 1e3) / 1e9
+    log(f"{R} x {args.steps} steps: median {ms_per_step * 1e3:.1f} us/step (blocks "
+        f"{', '.join(f'{b * 1e3 / args.steps:.1f}' for b in block_ms)}; host enqueue {host * 1e6 / args.steps:.1f} us/step, "
         f"wall {wall * 1e6 / args.steps:.1f} us/step), "
         f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s; "
-        f"path {'gemm' if gemm else 'gemv'}")
+        f"path {'gemm' if gemm else 'gemv'}; {ncopy} weight copies")
 
     lru_share = None
     if lru:
@@ -617,7 +647,10 @@ def run(args):
             key += "_" + flag
     kind = ("gemm_q" if mode == moe.MOE_MODE_B else "gemm") if gemm else "gemv"
     traffic = recorded_traffic(kind, key)
-    tflops = sum(gate_up_flops(i % len(rot)) for i in range(args.steps)) / (sum(gu_ms) / 1e3) / 1e12
+    tflops = sum(gate_up_flops(i % len(rot)) for i in step_ids) / (sum(gu_ms) / 1e3) / 1e12
+    # the whole expert FFN (gate/up + down) of the median block: algorithmic flops over the step
+    # time, i.e. with routing, permutation and combine counted as time
+    layer_tflops = sum(gate_up_flops(i % len(rot)) * 1.5 for i in med_ids) / (total_ms / 1e3) / 1e12
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": (("moe::gemm::gemm_q_kernel" if mode == moe.MOE_MODE_B else "moe::gemm::gemm_kernel")
@@ -642,10 +675,16 @@ def run(args):
         roofline["mfma_peak"] = MFMA_PEAK_TFLOPS[mfma_dt]
         roofline["mfma_frac"] = round(tflops / MFMA_PEAK_TFLOPS[mfma_dt], 4)
         roofline["mfma_frac_of_bf16_peak"] = round(tflops / MFMA_PEAK_TFLOPS["bf16"], 4)
+        roofline["layer_mfma_tflops"] = round(layer_tflops, 1)
+        roofline["layer_mfma_frac"] = round(layer_tflops / MFMA_PEAK_TFLOPS[mfma_dt], 4)
+    roofline["layer_hbm_frac"] = round(layer_gbs / HBM_PEAK_GBS, 4)
 
     cpu = None
     if args.cpu_baseline and not tiers:
-        cpu = cpu_baseline(cfg, rot, host_w, slot_map, args.cpu_seconds)
+        if T > 256:  # a prefill batch: the oracle runs the routing of the whole batch and the FFN of a token sample
+            cpu = cpu_baseline_sample(cfg, rot, host_w, slot_map, args.cpu_seconds)
+        else:
+            cpu = cpu_baseline(cfg, rot, host_w, slot_map, args.cpu_seconds)
 
     rec = {
         "metric": "MoE layer tokens/s",
@@ -654,6 +693,7 @@ def run(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "repeats": R,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -664,7 +704,8 @@ def run(args):
         "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} I={I} k={k} S={S} "
                                f"{cfg.score}-renorm weights={cfg.wdtype}"
                                + (f" + pool tier of {P} experts (miss rows computed, both tiers combined)" if tiers else ""),
-                   "tokens_per_step": T, "rotations": len(rot), "path": args.path, "mode": args.mode,
+                   "tokens_per_step": T, "rotations": len(rot), "weight_copies": ncopy,
+                   "path": args.path, "mode": args.mode,
                    "layer_algorithmic_GBs": round(layer_gbs, 1),
                    "touched_slots_per_step": round(float(np.mean([p[0] for p in per_rot])), 2),
                    "resident_row_share": round(lru_share if lru else float(np.mean([p[1] for p in per_rot])) / (T * k), 4),
@@ -672,11 +713,12 @@ def run(args):
                                 else "seeded, then LRU refill after every call" if lru
                                 else "seeded" if slot_map is not None else "all resident"),
                    "timing": (f"HIP graph of {graph['layers']} layers ({graph['weight_copies']} weight copies), "
-                              f"per-layer time of its replays" if graph else "eager launches; gate/up timed by fence-free HIP events")},
+                              f"per-layer time of its replays" if graph else
+                              f"eager launches; median of {R} blocks of {args.steps} steps; gate/up timed by fence-free HIP events")},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def cpu_baseline(cfg, rot, host_w, slot_map, budget_s):
@@ -715,6 +757,68 @@ def cpu_baseline(cfg, rot, host_w, slot_map, budget_s):
                       f"{spent:.1f} s"}
 
 
+def prefill_leg(r):
+    """The prefill numbers of a run's record: tokens/s, the gate/up GEMM's matrix-core rate and
+    HBM rate (with its counter record), the whole expert FFN's rate over the step time."""
+    rf = r["roofline"]
+    return {"workload": r["config"]["workload"], "mode": r["config"]["mode"], "value": r["value"],
+            "unit": r["unit"], "ms_per_step": r["ms_per_step"], "steps": r["steps"], "repeats": r["repeats"],
+            "weight_copies": r["config"]["weight_copies"], "dtype": r["dtype"],
+            "mfma_dtype": rf.get("mfma_dtype"), "mfma_peak": rf.get("mfma_peak"),
+            "gate_up": {k: rf.get(k) for k in ("kernel", "avg_launch_us", "mfma_tflops", "mfma_frac",
+                                               "mfma_frac_of_bf16_peak", "achieved", "frac", "bytes_per_launch",
+                                               "traffic", "traffic_vs_algorithmic", "traffic_agrees")},
+            "layer_mfma_tflops": rf.get("layer_mfma_tflops"), "layer_mfma_frac": rf.get("layer_mfma_frac"),
+            "layer_hbm_frac": rf.get("layer_hbm_frac"), "cpu_baseline": r["cpu_baseline"]}
+
+
+def cpu_baseline_sample(cfg, rot, host_w, slot_map, budget_s):
+    """Time the CPU oracle on a prefill batch, bounded: its routing and permutation of the whole
+    batch (timed once), and its expert FFN and combine on a token sample (4 tokens, doubled while
+    the budget allows).  Reported as the oracle's per-token rate 1 / (t_route / T + t_ffn / n):
+    the routing time spread over the batch plus the sample's FFN time per token."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    x, lg = rot[0]
+    args = (x, cfg.xdtype, host_w, cfg.wdtype, cfg.H, cfg.I, cfg.E, cfg.k, cfg.score, cfg.renorm)
+    t0 = time.perf_counter()
+    O.layer(*args, logits=lg, slot_map=slot_map, S=cfg.S, tokens=np.zeros(0, np.int64))
+    t_route = time.perf_counter() - t0
+    log(f"cpu oracle: routing and permutation of the {cfg.T}-token batch {t_route:.1f}s")
+    rng = np.random.default_rng(12345)
+    n, spent = 4, t_route
+    while True:
+        tokens = np.sort(rng.choice(cfg.T, size=min(n, cfg.T), replace=False))
+        t0 = time.perf_counter()
+        O.layer(*args, logits=lg, slot_map=slot_map, S=cfg.S, tokens=tokens)
+        dt = time.perf_counter() - t0
+        spent += dt
+        t_ffn = max(dt - t_route, 1e-9)
+        log(f"cpu oracle: {tokens.size}-token sample {dt:.1f}s (FFN and combine {t_ffn:.1f}s)")
+        if spent + 2 * dt > budget_s or n >= cfg.T:
+            break
+        n *= 2
+    rate = 1.0 / (t_route / cfg.T + t_ffn / tokens.size)
+    return {"value": round(rate, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "cpus_available": len(os.sched_getaffinity(0)),
+            "sample": f"fp64 oracle on the {cfg.T}-token batch: routing and permutation of all tokens "
+                      f"({t_route:.1f} s), expert FFN (per-slot dequantisation of the touched experts) and "
+                      f"combine of {tokens.size} sampled tokens ({t_ffn:.1f} s); rate = 1 / (routing time per "
+                      f"batch token + FFN time per sampled token)"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            return next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "unknown")
+    except OSError:  # pragma: no cover
+        return "unknown"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -723,7 +827,13 @@ def main(argv=None):
     ap.add_argument("--config", default="decode_bf16")
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=8)
-    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--repeats", type=int, default=5, help="timed blocks of --steps steps; the median is reported")
+    ap.add_argument("--weight-copies", type=int, default=0,
+                    help="device copies of the weights used in turn (0: enough for 1.5 GB between reuses)")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false",
+                    help="skip the prefill leg (the 4096-token FP8 batch, modes A and B) of the default run")
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm", "invariant"])
     ap.add_argument("--mode", default="A", choices=["A", "B"])
     ap.add_argument("--E", type=int, default=None, help="override the expert count of the config")
     ap.add_argument("--lru", action="store_true",
@@ -762,7 +872,27 @@ def main(argv=None):
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}, "
               f"WORLD_SIZE {world}). Run with --gpus 1.", file=sys.stderr)
         return 2
-    run(a)
+    rec = run(a)
+    if a.prefill and a.config == "decode_bf16" and a.T is None and a.E is None and not (
+            a.tiers or a.lru or a.plan_slots or a.graph_layers):
+        # the metric's prefill leg: the 4096-token chunk (FP8 weights, Zipf routing) on the matrix
+        # cores, mode A (bf16 MFMA) and mode B (block-scaled FP8 MFMA), in the same process
+        import gc
+        import torch
+        gc.collect()
+        torch.cuda.empty_cache()
+        legs = {}
+        for mode in ("A", "B"):
+            pa = argparse.Namespace(**vars(a))
+            pa.config, pa.mode, pa.path = "prefill_fp8_zipf", mode, "auto"
+            pa.steps, pa.warmup = a.prefill_steps, max(2, min(a.warmup, 5))
+            pa.cpu_baseline = a.cpu_baseline and mode == "A"
+            pa.copy_probe_mib = 0
+            legs[mode] = prefill_leg(run(pa))
+            gc.collect()
+            torch.cuda.empty_cache()
+        rec["prefill"] = dict(legs["A"], mode_b=legs["B"])
+    print(json.dumps(rec), flush=True)
     return 0
 
 

@@ -195,6 +195,19 @@ int moe_route_permute(const void* x, int x_dtype, int T, int H, const float* w_r
  * Positions whose perm entry names a token outside [0, T) are skipped.
  * ------------------------------------------------------------------------------------------ */
 size_t moe_expert_ffn_workspace_size(const moe_weights* w, int T, int k, int path, int mode);
+
+/* Where moe_expert_gate_up leaves the intermediate a in the expert-FFN workspace, for callers that
+ * inspect it (tests, debugging).  Fills, for the same (w, T, k, path, mode) as the call:
+ *   offsets[0]  byte offset of a: fp32 [T*k, I] on the GEMV path (mode B: the quantised values);
+ *               mode A on the GEMM path bf16 [T*k, I], or, where H*I >= 2^25, rows of 2I bf16
+ *               values (the I hi halves, then the I lo halves: a = hi + lo)
+ *   offsets[1]  byte offset of the E4M3 codes of a, uint8 [T*k, I] (mode B on the GEMM path)
+ *   offsets[2]  byte offset of their E8M0 scales, uint8 [T*k, I/32] (same)
+ *   offsets[3]  the format of a: 0 = fp32, 1 = bf16, 2 = bf16 (hi, lo) pairs, 3 = E4M3 + E8M0
+ * Rows are positions p < slot_offsets[S]; offsets that do not apply are (size_t)-1.  Returns
+ * MOE_OK, or MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as moe_expert_ffn would. */
+int moe_expert_ffn_workspace_layout(const moe_weights* w, int T, int k, int path, int mode, size_t offsets[4]);
+
 int moe_expert_ffn(const moe_weights* w, const void* x, int x_dtype, int T, int k,
                    const int32_t* perm, const int32_t* slot_offsets, int path, int mode,
                    float* y_perm, void* ws, size_t ws_bytes, void* stream);

@@ -56,6 +56,7 @@ _SIGS = {
     "moe_route_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _R, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _Z, _P]),
     "moe_expert_ffn_workspace_size": (_Z, [_W, _I, _I, _I, _I]),
+    "moe_expert_ffn_workspace_layout": (_I, [_W, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_expert_ffn": (_I, [_W, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_gate_up": (_I, [_W, _P, _I, _I, _I, _P, _P, _I, _I, _P, _Z, _P]),
     "moe_expert_down": (_I, [_W, _I, _I, _P, _I, _I, _P, _P, _Z, _P]),
@@ -187,6 +188,15 @@ def moe_route_permute(x, x_dtype, T, H, w_router, logits, bias, cfg, slot_map, S
 
 def moe_expert_ffn_workspace_size(w, T, k, path, mode) -> int:
     return lib().moe_expert_ffn_workspace_size(_ref(w), T, k, path, mode)
+
+
+def moe_expert_ffn_workspace_layout(w, T, k, path, mode):
+    """[offset of a, offset of its E4M3 codes, offset of their E8M0 scales, format of a] in the
+    expert-FFN workspace (offsets that do not apply are None)."""
+    off = (ctypes.c_size_t * 4)()
+    _check(lib().moe_expert_ffn_workspace_layout(_ref(w), T, k, path, mode, off), "moe_expert_ffn_workspace_layout")
+    none = (1 << (8 * ctypes.sizeof(ctypes.c_size_t))) - 1
+    return [None if v == none else int(v) for v in off[:3]] + [int(off[3])]
 
 
 def moe_resolve_path(w, T, k, path, mode) -> int:

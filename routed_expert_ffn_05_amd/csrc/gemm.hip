@@ -148,7 +148,8 @@ template <int WD, bool GATEUP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ wscale, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ perm, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, int S, int T, int k, int K, int N, int I, void* __restrict__ out) {
+    const int32_t* __restrict__ ntiles, int S, int T, int k, int K, int N, int I, int asplit,
+    void* __restrict__ out) {
   using F = BFmt<WD>;
   __shared__ __align__(16) uint8_t smem[F::BUDGET];
   __shared__ float Ssc[4][64];                                    // FP8 block scales
@@ -202,7 +203,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         src = m0 + r;
       }
     }
-    return reinterpret_cast<const uint8_t*>(act + size_t(src) * K) + swzA(r, lane % AGR) * 16;
+    // down with a split a: a row holds the hi halves of its I values, then the lo halves
+    return reinterpret_cast<const uint8_t*>(act + size_t(src) * K * (GATEUP ? 1 : asplit)) + swzA(r, lane % AGR) * 16;
   };
   // B: chunk c = INSTR*w + j covers 1 KiB of the tile: 128-byte rows, lane -> row 8c + lane/8
   // (bf16, FP8); 64-byte rows: lane -> row 16c + lane/4 (MXFP4)
@@ -277,7 +279,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   }
   const int fp4_row = bl * KB32, fp4_keyl = fp4_key(bl);
 
-  const int nk = K / BK;
+  // K steps: the weights' K once, or (down with a split a) twice, first against the hi halves of
+  // a, then against the lo halves; kwof(kk) is the weights' K step of step kk
+  const int nkw = K / BK;
+  const int nk = GATEUP ? nkw : nkw * asplit;
+  auto kwof = [&](int kk) -> int { return kk >= nkw ? kk - nkw : kk; };
 
   auto run = [&](auto ns_c) {
     constexpr int NS = decltype(ns_c)::value;
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       } else {
 #pragma unroll
         for (int q = 0; q < F::INSTR; ++q)
-          if (q == j - na) dma16(bsrc[q] + size_t(kk) * (F::ROW), st + AB + (F::INSTR * wv + q) * 1024);
+          if (q == j - na) dma16(bsrc[q] + size_t(kwof(kk)) * (F::ROW), st + AB + (F::INSTR * wv + q) * 1024);
       }
     };
     // the step's loads are spread over the first half of its K sub-steps (KG of them), so that
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         f.b[0] = q.x; f.b[1] = q.y;
       } else {  // 64-byte rows of 128 K: granule ks/2 holds K [32(ks/2), +32)
         f.b[0] = *reinterpret_cast<const uint32_t*>(B + bl * 64 + swz64(bl, ks >> 1) * 16 + (ks & 1) * 8 + kh * 4);
-        const int kb = kk * (BK / 32) + (ks >> 1);
+        const int kb = kwof(kk) * (BK / 32) + (ks >> 1);
         if (fp4_async) {
           int slot = (kb >> 4) + fp4_keyl;
           slot -= slot >= gpr ? gpr : 0;
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       }
       if constexpr (kBlockScaled) {
         // a step is one 128-wide K block: fold its partial sums in with the block's scale
-        const float sc = Ssc[srow][kk];
+        const float sc = Ssc[srow][kwof(kk)];
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms)
 #pragma unroll
@@ -465,16 +471,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
           const float recv = __shfl_xor(lo ? x1 : x0, 16);
           const float g = lo ? x0 : recv, u = lo ? recv : x1;
           const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3) + (lo ? 0 : 1);
-          if (m < rows) at[m * 128 + 16 * wv + (ln & 15)] = rowok[m] ? f32_to_bf16(silu_fast(g) * u) : uint16_t(0);
+          if (m < rows) {
+            const float a = rowok[m] ? silu_fast(g) * u : 0.0f;
+            const uint16_t hi = f32_to_bf16(a);
+            at[m * 128 + 16 * wv + (ln & 15)] = hi;
+            // split a: the rounding error of the hi half, itself rounded to bf16 (a to ~16 bits)
+            if (asplit == 2) at[BM * 128 + m * 128 + 16 * wv + (ln & 15)] = f32_to_bf16(a - bf16_to_f32(hi));
+          }
         }
       }
       __syncthreads();
       const int ncol = min(128, I - n0);  // columns of this tile (a multiple of 8)
-      for (int t = tid; t < rows * 16; t += kThreads) {
-        const int m = t >> 4, c8 = (t & 15) * 8;
+      const size_t ld = size_t(I) * asplit;  // a row: I values, or I hi halves then I lo halves
+      for (int t = tid; t < rows * 16 * asplit; t += kThreads) {
+        const int half = t / (rows * 16), tt = t - half * rows * 16;
+        const int m = tt >> 4, c8 = (tt & 15) * 8;
         if (c8 < ncol)
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + size_t(m0 + m) * I + n0 + c8) =
-              *reinterpret_cast<const uint4*>(at + m * 128 + c8);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + size_t(m0 + m) * ld + size_t(half) * I + n0 + c8) =
+              *reinterpret_cast<const uint4*>(at + half * BM * 128 + m * 128 + c8);
       }
     } else {
       store_y_tile<NS>(acc, smem, static_cast<float*>(out), m0, rows, n0, N);
@@ -1099,7 +1113,7 @@ static hipError_t gate_up_t(const GemmArgs& g, hipStream_t st) {
   }
   gemm::gemm_kernel<WD, true><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
       static_cast<const uint8_t*>(g.w_gu), g.s_gu, static_cast<const uint16_t*>(x), g.perm, g.tiles_gu,
-      g.counts, g.S, g.T, g.k, g.H, 2 * g.I, g.I, g.a);
+      g.counts, g.S, g.T, g.k, g.H, 2 * g.I, g.I, g.asplit, g.a);
   return hipGetLastError();
 }
 
@@ -1109,7 +1123,7 @@ static hipError_t down_t(const GemmArgs& g, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   gemm::gemm_kernel<WD, false><<<dim3(unsigned(grid)), dim3(gemm::kThreads), 0, st>>>(
       static_cast<const uint8_t*>(g.w_d), g.s_d, static_cast<const uint16_t*>(g.a), nullptr, g.tiles_dn,
-      g.counts + 8, g.S, g.T, g.k, g.I, g.H, g.I, g.y);
+      g.counts + 8, g.S, g.T, g.k, g.I, g.H, g.I, g.asplit, g.y);
   return hipGetLastError();
 }
 

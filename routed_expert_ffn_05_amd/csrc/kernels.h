@@ -66,6 +66,7 @@ struct GemmArgs {
   int4* tiles_dn;
   int32_t* counts;      // [16]: tiles per XCD of the gate/up GEMM, then of the down GEMM
   bool tiles_contiguous;  // deal the tiles in (slot, M tile, N tile) order in eight runs
+  int asplit;             // mode A: 1 = a in bf16; 2 = a as a bf16 (hi, lo) pair, rows of 2I values
 };
 size_t gemm_tiles_max(int T, int k, int S, int nt);
 // entries of a GEMM's tile list (eight per-XCD lists of gemm_tile_slots / 8) = its launch grid

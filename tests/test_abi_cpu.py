@@ -235,3 +235,32 @@ def test_invariant_path_and_tile_order_flag(L):
     assert rp(w("bf16", 384), 4096, INV, mode=moe.MOE_MODE_B) == GEMV
     assert rp(w("fp8", 384), 1, INV, mode=moe.MOE_MODE_B) == GEMM
     assert rp(w("fp8", 384), 4, 0x200 | GEMM) == -1 and rp(w("fp8", 384), 4, C | 7) == -1
+
+
+def test_ffn_workspace_layout(L):
+    """Where the intermediate a lives in the expert-FFN workspace (host logic only): its format by
+    path and mode, 256-byte aligned offsets whose regions fit in the workspace size."""
+    def w(dt, S, H=4096, I=1024):
+        return moe.weights(dt, S, H, I, FAKE, FAKE, FAKE, FAKE)
+    A, B = moe.MOE_MODE_A, moe.MOE_MODE_B
+    T, k = 4096, 8
+    R = T * k
+    for wd, path, mode, fmt in ((w("fp8", 384), moe.MOE_PATH_GEMM, A, 1), (w("fp8", 384), moe.MOE_PATH_GEMM, B, 3),
+                                (w("fp8", 384), moe.MOE_PATH_GEMV, A, 0), (w("fp8", 384), moe.MOE_PATH_GEMV, B, 0),
+                                (w("bf16", 8, 8192, 8192), moe.MOE_PATH_GEMM, A, 2),
+                                (w("fp8", 8, 8192, 4096), moe.MOE_PATH_GEMM, A, 2),
+                                (w("fp8", 8, 4096, 8192), moe.MOE_PATH_GEMM, A, 2),
+                                (w("fp8", 8, 8192, 2048), moe.MOE_PATH_GEMM, A, 1),
+                                (w("mxfp4", 110), moe.MOE_PATH_AUTO, B, 3)):
+        off_a, off_q, off_s, f = moe.moe_expert_ffn_workspace_layout(wd, T, k, path, mode)
+        size = moe.moe_expert_ffn_workspace_size(wd, T, k, path, mode)
+        I = wd.I
+        assert f == fmt, (wd.wdtype, path, mode, f)
+        if f == 3:
+            assert off_a is None and off_q % 256 == 0 and off_s % 256 == 0
+            assert off_q + R * I <= off_s and off_s + R * I // 32 <= size
+        else:
+            assert off_q is None and off_s is None and off_a % 256 == 0
+            assert off_a + R * I * (4 if f in (0, 2) else 2) <= size
+    with pytest.raises(moe.MoeError):
+        moe.moe_expert_ffn_workspace_layout(w("fp8", 384), T, k, 9, A)

@@ -159,7 +159,9 @@ class GpuCase:
                        miss_weight=D.to_host(mw)[:n_miss])
         return res
 
-    def expert_ffn(self, perm, slot_offsets, path=moe.MOE_PATH_AUTO, mode=moe.MOE_MODE_A):
+    def expert_ffn(self, perm, slot_offsets, path=moe.MOE_PATH_AUTO, mode=moe.MOE_MODE_A, want_a=False):
+        """y_perm rows of the call; with want_a also the intermediate a the call left in its
+        workspace (read through moe_expert_ffn_workspace_layout, as fp64 values)."""
         torch = self.torch
         c = self.cfg
         R = c.T * c.k
@@ -171,7 +173,11 @@ class GpuCase:
         ws = D.workspace(nb)
         moe.moe_expert_ffn(desc, self.x, self.xdt, c.T, c.k, d_perm, d_off, path, mode, y, ws, nb)
         torch.cuda.synchronize()
-        return D.to_host(y)[: len(perm)]
+        y = D.to_host(y)[: len(perm)]
+        if not want_a:
+            return y
+        return y, read_a(ws, moe.moe_expert_ffn_workspace_layout(desc, c.T, c.k, path, mode), len(perm), c.I)
+
 
     def combine(self, y_perm, inv_perm, topk_w):
         torch = self.torch
@@ -201,6 +207,92 @@ class GpuCase:
         torch.cuda.synchronize()
         o = D.to_host(out)
         return (D.bf16_bits_to_float(o) if self.odt == moe.MOE_BF16 else o).astype(np.float64)
+
+
+def read_a(ws, layout, n, I):
+    """The intermediate a of n permuted rows from an expert-FFN workspace (a torch uint8 tensor),
+    decoded to fp64 by its format (fp32; bf16; bf16 hi + lo; E4M3 codes x 2^(E8M0 - 127))."""
+    off_a, off_q, off_s, fmt = layout
+    host = D.to_host(ws)
+    if fmt == 0:
+        return host[off_a:off_a + n * I * 4].view(np.float32).reshape(n, I).astype(np.float64)
+    if fmt == 1:
+        return O.bf16_to_f64(host[off_a:off_a + n * I * 2].view(np.uint16).reshape(n, I))
+    if fmt == 2:
+        v = O.bf16_to_f64(host[off_a:off_a + n * 2 * I * 2].view(np.uint16).reshape(n, 2 * I))
+        return v[:, :I] + v[:, I:]
+    codes = host[off_q:off_q + n * I].reshape(n, I)
+    sc = host[off_s:off_s + n * (I // 32)].reshape(n, I // 32).astype(np.int64) - 127
+    return O.e4m3fn_to_f64(codes) * np.exp2(np.repeat(sc, 32, axis=1))
+
+
+def oracle_mode_b_stages(inp, perm, off, positions, a_gpu, threads=1):
+    """The oracle's mode-B stages for the permuted rows `positions`, computed slot by slot from its
+    own primitives: the fp64 a of each row (from the MX-E4M3-quantised x, as the mirror does), its
+    MX-E4M3 quantisation (scale exponents and dequantised values), and the down projection applied
+    to the GPU's own quantised a (a_gpu, one row per position).  The quantisation of a is a
+    floating-point decision on an integer code: where the oracle's fp64 a and the kernel's fp32 a
+    straddle a rounding boundary both codes are correct, so the down projection is checked on the
+    GPU's codes and the codes are checked apart (check_mode_b_codes)."""
+    from concurrent.futures import ThreadPoolExecutor
+    cfg = inp.cfg
+    x64 = O.activations_f64(inp.x, cfg.xdtype)
+    positions = np.asarray(positions, np.int64)
+    slot_of = np.searchsorted(np.asarray(off), positions, side="right") - 1
+    res = dict(a64=np.empty((positions.size, cfg.I)), deq=np.empty((positions.size, cfg.I)),
+               X=np.empty((positions.size, cfg.I // 32), np.int64), y=np.empty((positions.size, cfg.H)))
+
+    def work(s):
+        sel = np.nonzero(slot_of == s)[0]
+        wg, wu, wd = O.slot_matrices(inp.weights, cfg.wdtype, int(s), cfg.H, cfg.I)
+        xq = O.act_quant_mx_e4m3(x64[np.asarray(perm)[positions[sel]] // cfg.k])
+        a64 = O.silu(xq @ wg.T) * (xq @ wu.T)
+        X, q = O.act_quant_mx_e4m3_parts(a64)
+        res["a64"][sel] = a64
+        res["X"][sel] = X
+        res["deq"][sel] = np.ldexp(q.reshape(sel.size, -1, 32), X[:, :, None]).reshape(sel.size, cfg.I)
+        res["y"][sel] = a_gpu[sel] @ wd.T
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(work, np.unique(slot_of)))
+    return res
+
+
+def check_mode_b_codes(a_gpu, st, what, rel=1e-3, rel_blk=1e-4):
+    """The GPU's quantised a against the oracle's exact (fp64) a.  The quantisation is a
+    floating-point decision on integer codes, taken by the kernel on its own fp32 a (block-scaled
+    matrix-core sums), which differs from the exact a by a little: allowed here up to
+    eps = rel*|a| + rel_blk*max|a| over the 32-value block (measured: about 2e-5 of the block
+    maximum).  Every GPU value must be the correct MX-E4M3 rounding of some value within eps of the
+    exact a: at the block's scale exponent, or one higher or lower where the block maximum itself
+    lies within eps_blk of a power of two.  Returns the share of values equal to the oracle's own
+    quantisation (information)."""
+    a64, X = st["a64"], st["X"]
+    n, K = a64.shape
+    blk = np.abs(a64).reshape(n, K // 32, 32).max(axis=2)
+    eps = rel * np.abs(a64) + np.repeat(rel_blk * blk, 32, axis=1)
+    eps_blk = (rel + rel_blk) * blk
+    valid = np.zeros(a64.shape, bool)
+    for dx in (-1, 0, 1):
+        Xc = X + dx
+        if dx:  # another scale only where the block maximum's binade is ambiguous
+            ok = (np.floor(np.log2(np.maximum(blk - eps_blk, 1e-300))) !=
+                  np.floor(np.log2(np.maximum(blk + eps_blk, 1e-300))))
+            ok &= blk > 0
+            if not ok.any():
+                continue
+        else:
+            ok = np.ones_like(blk, bool)
+        sc = np.repeat(Xc, 32, axis=1)
+        lo = np.ldexp(O.e4m3fn_round(np.ldexp(a64 - eps, -sc)), sc)
+        hi = np.ldexp(O.e4m3fn_round(np.ldexp(a64 + eps, -sc)), sc)
+        valid |= np.repeat(ok, 32, axis=1) & (lo <= a_gpu) & (a_gpu <= hi)
+    if not valid.all():
+        ii = np.argwhere(~valid)[:6]
+        ex = "; ".join(f"row {r} col {c}: exact {a64[r, c]:.6g} gpu {a_gpu[r, c]:.6g} oracle {st['deq'][r, c]:.6g} "
+                       f"X {X[r, c // 32]} block max {blk[r, c // 32]:.6g}" for r, c in ii)
+        raise AssertionError(f"{what}: {(~valid).sum()} quantised a values that no value within the kernel's "
+                             f"precision of the exact a rounds to: {ex}")
+    return float((a_gpu == st["deq"]).mean()) if a_gpu.size else 1.0
 
 
 def routing_mismatches(gpu_idx, ref):

@@ -6,7 +6,10 @@ output element of the GEMV and the GEMM is reduced in a fixed order whatever oth
 slot or tile, and the combine is per token.
 
 One probe token is placed at several positions of batches from 1 to 300 tokens (other tokens
-random); its output row must be the same bits in every batch, for each path and mode."""
+random); its output row must be the same bits in every batch, for each path and mode -- including
+MOE_PATH_INVARIANT, the batch-invariant choice for callers that want the matrix cores wherever the
+shape allows: the batches cross AUTO's GEMV/GEMM crossover (T*k = c*S with S = 16: T = 11 for bf16,
+8 for FP8, 2 for MXFP4), and INVARIANT stays on one path across all of them."""
 import dataclasses
 import sys
 
@@ -26,7 +29,8 @@ def _batch(cfg, T, pos, pool):
     return x
 
 
-@pytest.mark.parametrize("path,mode", [("gemv", "A"), ("gemm", "A"), ("gemv", "B"), ("gemm", "B")])
+@pytest.mark.parametrize("path,mode", [("gemv", "A"), ("gemm", "A"), ("gemv", "B"), ("gemm", "B"),
+                                       ("invariant", "A"), ("invariant", "B")])
 @pytest.mark.parametrize("wd", ["bf16", "fp8", "mxfp4"])
 def test_probe_token_output_is_batch_invariant(path, mode, wd):
     import torch
@@ -41,7 +45,7 @@ def test_probe_token_output_is_batch_invariant(path, mode, wd):
     inp0 = gen.make_inputs(base)
     pool = inp0.x                                    # 301 tokens: the probe is row 0
     w_dev = D.upload_weights(wd, base.H, base.I, inp0.weights)
-    p = moe.MOE_PATH_GEMV if path == "gemv" else moe.MOE_PATH_GEMM
+    p = {"gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM, "invariant": moe.MOE_PATH_INVARIANT}[path]
     m = moe.MOE_MODE_A if mode == "A" else moe.MOE_MODE_B
     ref = None
     for T, pos in SIZES:

@@ -1,10 +1,22 @@
 """Full-size parity: every workload at its stated size, run through the same C-ABI call sequence
 that bench.py times (route+permute, gate/up, down, combine on one stream, device-resident inputs),
-checked against the oracle: routing, counts, slot offsets, permutation and the compact miss list
-in full; the expert-FFN rows and layer outputs of a seeded sample of tokens (the oracle computes
-only those tokens' rows, dequantising just the experts they touch)."""
+checked against the oracle:
+
+* routing of every token (near-ties reported apart), and counts, slot offsets, permutation and the
+  compact miss list in full -- bit for bit against the oracle's permutation of the GPU's own routing,
+  so that a legitimate near-tie flip never skips these checks (and against the oracle's routing
+  when there is none);
+* expert-FFN rows, stratified: at least one row of every (slot, 128-row M tile) -- every GEMM tile
+  of both projections, wherever the scheduler placed it -- plus every row of the hottest slot's
+  first and last scheduling unit (four M tiles), each against the oracle FFN of that row's slot and
+  token;
+* layer outputs of a seeded sample of tokens.
+
+The oracle's per-slot work is spread over host threads (slots are independent)."""
+import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -16,14 +28,60 @@ pytestmark = pytest.mark.gpu
 FULL = [("decode_bf16", None, "A"), ("decode_fp8", None, "A"), ("prefill_fp8_zipf", None, "A"),
         ("compact_mxfp4", 1, "A"), ("compact_mxfp4", 4096, "A"),
         # mode B on the block-scaled matrix cores, against the oracle with the same activation
-        # quantisation (the scale-aware bound widened as in the small mode-B cases)
+        # quantisation, stage by stage (the quantised a, then y from the GPU's quantised a)
         ("prefill_fp8_zipf", None, "B"), ("compact_mxfp4", 4096, "B")]
-N_SAMPLE = 4
+N_SAMPLE = 16
+BM = 128          # rows per GEMM M tile
+UNIT_M = 4        # M tiles per scheduling unit
 
 
 def _say(msg):
     print(f"[gpu-full] {msg}", flush=True)
     sys.stdout.flush()
+
+
+def stratified_positions(off, rng):
+    """Positions (in the permuted row order) to check: one random row of every 128-row M tile of
+    every slot, and every row of the hottest slot's first and last unit of four M tiles."""
+    off = np.asarray(off, np.int64)
+    pos = []
+    for s in range(off.size - 1):
+        lo, hi = int(off[s]), int(off[s + 1])
+        for m0 in range(lo, hi, BM):
+            pos.append(int(rng.integers(m0, min(m0 + BM, hi))))
+    sizes = np.diff(off)
+    if sizes.size and sizes.max() > 0:
+        s = int(np.argmax(sizes))
+        lo, hi = int(off[s]), int(off[s + 1])
+        n_mt = -(-(hi - lo) // BM)
+        last_unit = ((n_mt - 1) // UNIT_M) * UNIT_M
+        pos.extend(range(lo, min(hi, lo + UNIT_M * BM)))
+        pos.extend(range(lo + last_unit * BM, hi))
+    return np.unique(np.asarray(pos, np.int64))
+
+
+def oracle_rows(O, inp, perm, off, positions, act_quant, threads):
+    """The oracle's y_perm rows at `positions` (NaN elsewhere), slots spread over host threads."""
+    cfg = inp.cfg
+    x64 = O.activations_f64(inp.x, cfg.xdtype)
+    mask = np.zeros(perm.size, bool)
+    mask[positions] = True
+    slot_of = np.repeat(np.arange(off.size - 1), np.diff(off))
+    parts = []
+
+    def work(t):
+        m = mask & (slot_of % threads == t)
+        if not m.any():
+            return None
+        return O.expert_ffn(inp.weights, cfg.wdtype, x64, perm, off, cfg.k, cfg.H, cfg.I, positions=m,
+                            act_quant=act_quant)
+    with ThreadPoolExecutor(threads) as ex:
+        parts = [p for p in ex.map(work, range(threads)) if p is not None]
+    y = np.full((perm.size, cfg.H), np.nan)
+    for p in parts:
+        ok = ~np.isnan(p[:, 0])
+        y[ok] = p[ok]
+    return y
 
 
 def _run_staged(inp, w, mode):
@@ -70,7 +128,8 @@ def _run_staged(inp, w, mode):
     moe.moe_check_device_error(pws)
     n_res = int(D.to_host(off)[-1])
     res = dict(topk_idx=D.to_host(idx), topk_w=D.to_host(tw), counts=D.to_host(counts), slot_offsets=D.to_host(off),
-               perm=D.to_host(perm)[:n_res], inv_perm=D.to_host(inv), y=y, out=out, odt=odt)
+               perm=D.to_host(perm)[:n_res], inv_perm=D.to_host(inv), y=y, out=out, odt=odt, fws=fws,
+               layout=moe.moe_expert_ffn_workspace_layout(w.desc, T, k, path, mode))
     if c:
         n = int(D.to_host(mc)[0])
         res.update(miss_count=n, miss_token=D.to_host(mt)[:n], miss_expert=D.to_host(me)[:n],
@@ -85,7 +144,8 @@ def test_full_size_layer(name, T, mode):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import routed_expert_ffn_05_amd as moe
-    from gpu_cases import assert_fp_close, check_permute, check_routing
+    from gpu_cases import (assert_fp_close, check_mode_b_codes, check_permute, check_routing, oracle_mode_b_stages,
+                           read_a)
     from oracle import moe_oracle as O
     from routed_expert_ffn_05_amd import device as D
     cfg = gen.config(name, T=T) if T else gen.config(name)
@@ -95,29 +155,63 @@ def test_full_size_layer(name, T, mode):
     _say(f"{name}: inputs in {time.time() - t0:.1f}s; uploading")
     w = D.upload_weights(cfg.wdtype, cfg.H, cfg.I, inp.weights)
     res = _run_staged(inp, w, moe.MOE_MODE_A if mode == "A" else moe.MOE_MODE_B)
-    _say(f"{name}: GPU layer done; oracle on a sample")
+    act_quant = O.act_quant_mx_e4m3 if mode == "B" else None
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
     rng = np.random.default_rng(1234)
     sample = np.sort(rng.choice(cfg.T, size=min(N_SAMPLE, cfg.T), replace=False))
+    _say(f"{name}: GPU layer done; oracle routing and permutation")
     t0 = time.time()
     ref = O.layer(inp.x, cfg.xdtype, inp.weights, cfg.wdtype, cfg.H, cfg.I, cfg.E, cfg.k, cfg.score, cfg.renorm,
-                  w_router=inp.w_router, logits=inp.logits, slot_map=inp.slot_map, S=cfg.S, tokens=sample,
-                  act_quant=O.act_quant_mx_e4m3 if mode == "B" else None)
-    stol = 8e-2 if mode == "B" else 2e-2
-    _say(f"{name}: oracle in {time.time() - t0:.1f}s")
-    # routing and permutation, every token
+                  w_router=inp.w_router, logits=inp.logits, slot_map=inp.slot_map, S=cfg.S,
+                  tokens=np.zeros(0, np.int64))
+    _say(f"{name}: oracle routing in {time.time() - t0:.1f}s")
+    # routing of every token; near-ties may flip
     flipped = check_routing(res["topk_idx"], res["topk_w"], ref)
     if not flipped:
         check_permute(res, ref)
-    # sampled tokens: their expert-FFN rows and outputs
+    # the permutation and miss list of the GPU's own routing, always, bit for bit
+    g_idx, g_w = res["topk_idx"], res["topk_w"]
+    own = dict(counts=O.histogram(g_idx, cfg.E))
+    own["slot_offsets"], own["perm"], own["inv_perm"] = O.permute(g_idx, inp.slot_map, cfg.S)
+    check_permute({k_: res[k_] for k_ in ("counts", "slot_offsets", "perm", "inv_perm")}, own)
+    if inp.slot_map is not None:
+        mt_, me_, _ = O.miss_list(g_idx, g_w, inp.slot_map)
+        assert res["miss_count"] == mt_.size
+        assert np.array_equal(res["miss_token"], mt_) and np.array_equal(res["miss_expert"], me_)
+        r = np.nonzero(np.asarray(inp.slot_map)[g_idx.reshape(-1)] < 0)[0]  # the miss rows, ascending
+        assert np.array_equal(res["miss_weight"].view(np.uint32), g_w.reshape(-1)[r].view(np.uint32)), \
+            "miss weights are the GPU's own gates, copied"
+    # expert-FFN rows, stratified over every (slot, M tile), and the rows of the sampled tokens (not
+    # near-tie flips), against the oracle FFN of each row's slot and token; the GPU's permutation,
+    # checked above, names both
+    off, perm, inv = own["slot_offsets"], own["perm"], own["inv_perm"]
     keep = np.array([t not in flipped for t in sample], bool)
     assert keep.any()
     tok = sample[keep]
-    pos = ref["inv_perm"].reshape(cfg.T, cfg.k)[tok].reshape(-1)
-    pos = pos[pos >= 0]
-    if pos.size:
-        y_gpu = D.to_host(res["y"][torch.as_tensor(pos, device="cuda").long()]).astype(np.float64)
-        assert_fp_close(y_gpu, ref["y_perm"][pos], f"{name} y_perm rows of the sample", scale_tol=stol)
+    tok_pos = inv.reshape(cfg.T, cfg.k)[tok].reshape(-1)
+    strat = stratified_positions(off, rng)
+    pos = np.union1d(strat, tok_pos[tok_pos >= 0])
+    t0 = time.time()
+    if mode == "A":
+        y_all = oracle_rows(O, inp, perm, off, pos, act_quant, threads)
+    else:
+        # mode B: the quantised a checked apart, y against the oracle's down projection of the
+        # GPU's own quantised a (both codes of a rounding-boundary case are correct)
+        a_gpu = read_a(res["fws"], res["layout"], perm.size, cfg.I)[pos]
+        st = oracle_mode_b_stages(inp, perm, off, pos, a_gpu, threads)
+        frac = check_mode_b_codes(a_gpu, st, f"{name} quantised a of {pos.size} rows")
+        _say(f"{name}: quantised a equal to the oracle's for {frac:.5f} of {a_gpu.size} values")
+        y_all = np.full((perm.size, cfg.H), np.nan)
+        y_all[pos] = st["y"]
+    _say(f"{name}: oracle FFN of {pos.size} rows ({strat.size} stratified over {np.count_nonzero(np.diff(off))} "
+         f"slots) in {time.time() - t0:.1f}s on {threads} threads")
+    if strat.size:
+        y_gpu = D.to_host(res["y"][torch.as_tensor(strat, device="cuda").long()]).astype(np.float64)
+        assert_fp_close(y_gpu, y_all[strat], f"{name} y_perm, one row per (slot, M tile) + hottest slot's end units")
+    # sampled tokens: layer outputs, the oracle's combine of the oracle rows with the oracle's gates
+    sub_inv = inv.reshape(cfg.T, cfg.k)[tok].reshape(-1)
+    ref_out = O.combine(y_all, sub_inv, np.asarray(ref["topk_w"]).reshape(cfg.T, cfg.k)[tok], tok.size, cfg.k, cfg.H)
     o = D.to_host(res["out"][torch.as_tensor(tok, device="cuda").long()])
     o = (D.bf16_bits_to_float(o) if res["odt"] == moe.MOE_BF16 else o).astype(np.float64)
-    assert_fp_close(o, ref["out"][keep], f"{name} out rows of the sample", scale_tol=stol)
-    _say(f"{name}: ok ({len(tok)} sampled tokens, {pos.size} expert rows, {len(flipped)} near-tie flips)")
+    assert_fp_close(o, ref_out, f"{name} out rows of the sample")
+    _say(f"{name}: ok ({strat.size} stratified rows, {len(tok)} sampled tokens, {len(flipped)} near-tie flips)")

@@ -12,12 +12,13 @@ from synth import gen
 
 pytestmark = pytest.mark.gpu
 
-# The block-scaled matrix cores do not accumulate a 64-wide product exactly in fp32 (sums of
-# E4M3 products that fp32 holds exactly come back with relative errors up to a few 1e-3), and the
-# second quantisation (of a, before down) turns such an error into a one-step E4M3 change of an
-# element now and then.  The stated bar (elementwise 2e-2*max(1,|ref|), relative L2 5e-3) holds;
-# the extra scale-aware elementwise bound is widened from 2e-2 to 8e-2 of max(|ref|, rms) on that
-# path only.
+# The activation quantisation is a floating-point decision on integer codes: where the kernel's
+# fp32 a and the oracle's fp64 a straddle an E4M3 rounding boundary, both codes are correct.  The
+# expert-FFN stage is therefore checked in two parts (gpu_cases.oracle_mode_b_stages): the GPU's
+# quantised a against the oracle's (equal but for boundary cases, each within one E4M3 step), and
+# y against the oracle's down projection of the GPU's own quantised a, at the stated bar.  The
+# whole-layer test compares with the mirror end to end; its extra scale-aware bound (not part of
+# the stated bar) is 8e-2 of max(|ref|, rms), for the boundary cases.
 GEMM_SCALE_TOL = 8e-2
 
 CASES = {
@@ -119,7 +120,7 @@ def test_quantizer_bit_exact():
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
 def test_mode_b_expert_ffn(case, path):
     import routed_expert_ffn_05_amd as moe
-    from gpu_cases import assert_fp_close
+    from gpu_cases import assert_fp_close, check_mode_b_codes, oracle_mode_b_stages
     name, inp, g, ref, plain = case
     _banner(f"{name}/expert_ffn/{path}")
     p = moe.MOE_PATH_GEMV if path == "gemv" else moe.MOE_PATH_GEMM
@@ -128,14 +129,17 @@ def test_mode_b_expert_ffn(case, path):
             g.expert_ffn(ref["perm"], ref["slot_offsets"], path=p, mode=moe.MOE_MODE_B)
         assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
         return
-    y = g.expert_ffn(ref["perm"], ref["slot_offsets"], path=p, mode=moe.MOE_MODE_B)
-    assert_fp_close(y, ref["y_perm"], f"{name} y_perm (mode B, {path})",
-                    scale_tol=GEMM_SCALE_TOL if path == "gemm" else 2e-2)
-    # information: mode B against the unquantised oracle
-    n = np.linalg.norm(plain["y_perm"])
-    if n > 0:
-        print(f"[gpu-mode-b] {name} {path}: mode B vs plain oracle relative L2 "
-              f"{np.linalg.norm(y - plain['y_perm']) / n:.3g}")
+    y, a = g.expert_ffn(ref["perm"], ref["slot_offsets"], path=p, mode=moe.MOE_MODE_B, want_a=True)
+    n = len(ref["perm"])
+    st = oracle_mode_b_stages(inp, ref["perm"], ref["slot_offsets"], np.arange(n), a, threads=8)
+    frac = check_mode_b_codes(a, st, f"{name} quantised a (mode B, {path})")
+    assert_fp_close(y, st["y"], f"{name} y_perm from the GPU's quantised a (mode B, {path})")
+    # information: end to end against the mirror, and mode B against the unquantised oracle
+    nrm = np.linalg.norm(plain["y_perm"])
+    if nrm > 0:
+        print(f"[gpu-mode-b] {name} {path}: quantised a equal to the oracle's for {frac:.5f} of the values; "
+              f"y vs mirror rel L2 {np.linalg.norm(y - ref['y_perm']) / np.linalg.norm(ref['y_perm']):.3g}; "
+              f"mode B vs plain oracle rel L2 {np.linalg.norm(y - plain['y_perm']) / nrm:.3g}")
 
 
 def test_mode_b_layer(case):

@@ -268,6 +268,26 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
               void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_layer_static -- moe_layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that forbid allocation): the same arguments and results without
+ * ws / ws_bytes; the workspace is a static array of MOE_STATIC_WORKSPACE_BYTES in the library,
+ * one per GPU, held until the process ends.  Nothing is allocated or freed.
+ *   Limit: moe_layer_workspace_size() of the call must be at most MOE_STATIC_WORKSPACE_BYTES
+ *   (32 MiB: at H = 4096, I = 1024, k = 8 up to 192 tokens), else MOE_ERR_UNSUPPORTED and
+ *   nothing is enqueued.
+ *   Every call on a GPU uses that GPU's one array: calls that overlap on one GPU (other streams,
+ *   other threads) race and must be ordered by the caller.  The array keeps the last call's
+ *   contents; nothing in it needs to start at zero (each call writes what it reads, the device
+ *   error word included), and moe_check_device_error cannot be pointed at it.
+ * ------------------------------------------------------------------------------------------ */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+int moe_layer_static(const void* x, int x_dtype, int T, const float* w_router, const float* logits,
+                     const float* bias, const moe_routing* cfg, const int32_t* slot_map,
+                     const moe_weights* w, int path, int mode, void* out, int out_dtype,
+                     int32_t* topk_idx, float* topk_w, int32_t* miss_count, int32_t* miss_token,
+                     int32_t* miss_expert, float* miss_weight, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_quantize_mx_e4m3 -- the mode-B activation quantisation, on its own (OCP MX rule with an
  * E4M3 element type).  For each row and each 32 consecutive elements: X = floor(log2 amax) - 8
  * (X = 0 for an all-zero block; X is kept >= -127), scale byte X + 127 (E8M0), codes = E4M3

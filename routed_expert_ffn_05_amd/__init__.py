@@ -69,6 +69,7 @@ _SIGS = {
     "moe_layer_workspace_size": (_Z, [_I, _R, _W, _I, _I, _I]),
     "moe_layer": (_I, [_P, _I, _I, _P, _P, _P, _R, _P, _W, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                        _P, _Z, _P]),
+    "moe_layer_static": (_I, [_P, _I, _I, _P, _P, _P, _R, _P, _W, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_mx_e4m3": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P]),
     "moe_check_device_error": (_I, [_P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
@@ -262,6 +263,17 @@ def moe_layer(x, x_dtype, T, w_router, logits, bias, cfg, slot_map, w, path, mod
                            _ptr(slot_map), _ref(w), path, mode, _ptr(out), out_dtype, _ptr(topk_idx),
                            _ptr(topk_w), _ptr(miss_count), _ptr(miss_token), _ptr(miss_expert),
                            _ptr(miss_weight), _ptr(ws), ws_bytes, _stream(stream)), "moe_layer")
+
+
+MOE_STATIC_WORKSPACE_BYTES = 32 << 20
+
+
+def moe_layer_static(x, x_dtype, T, w_router, logits, bias, cfg, slot_map, w, path, mode, out, out_dtype,
+                     topk_idx, topk_w, miss_count, miss_token, miss_expert, miss_weight, stream=None):
+    _check(lib().moe_layer_static(_ptr(x), x_dtype, T, _ptr(w_router), _ptr(logits), _ptr(bias), _ref(cfg),
+                                  _ptr(slot_map), _ref(w), path, mode, _ptr(out), out_dtype, _ptr(topk_idx),
+                                  _ptr(topk_w), _ptr(miss_count), _ptr(miss_token), _ptr(miss_expert),
+                                  _ptr(miss_weight), _stream(stream)), "moe_layer_static")
 
 
 def moe_check_device_error(ws, stream=None):

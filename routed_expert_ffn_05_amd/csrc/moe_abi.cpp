@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
@@ -651,6 +652,51 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
   MOE_TRY(moe_expert_ffn(w, x, x_dtype, T, cfg->k, L.perm, L.offsets, rp | (path & MOE_PATH_TILES_CONTIGUOUS), mode,
                          L.y, L.ffn, ffn_bytes, stream));
   return moe_combine(L.y, L.inv, tw, T, cfg->k, w->H, out, out_dtype, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// moe_layer_static: moe_layer on a workspace the library holds, for callers that cannot allocate.
+// The array below is the workspace of every call on a GPU; each GPU holds its own copy at its own
+// address, which the host looks up once per device (with that device current) and keeps.  In host
+// code the array's name is not a device address: only the looked-up pointer is used.
+namespace {
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_WORKSPACE_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_on_current_device(void** p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static workspace");
+    if (!ptr || !aligned(ptr, 256)) return fail(MOE_ERR_HIP, "static workspace at a misaligned address");
+    g_scratch[dev] = ptr;
+  }
+  *p = g_scratch[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_layer_static(const void* x, int x_dtype, int T, const float* w_router, const float* logits,
+                     const float* bias, const moe_routing* cfg, const int32_t* slot_map,
+                     const moe_weights* w, int path, int mode, void* out, int out_dtype,
+                     int32_t* topk_idx, float* topk_w, int32_t* miss_count, int32_t* miss_token,
+                     int32_t* miss_expert, float* miss_weight, void* stream) {
+  if (!cfg || !w) return fail(MOE_ERR_INVALID_ARG, "cfg / w is NULL");
+  const size_t need = moe_layer_workspace_size(T, cfg, w, path, mode, w_router != nullptr);
+  if (need > MOE_STATIC_WORKSPACE_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_layer_static: the call needs %zu bytes of workspace, the static one holds %zu",
+                need, size_t(MOE_STATIC_WORKSPACE_BYTES));
+  void* ws = nullptr;
+  MOE_TRY(scratch_on_current_device(&ws));
+  return moe_layer(x, x_dtype, T, w_router, logits, bias, cfg, slot_map, w, path, mode, out, out_dtype, topk_idx,
+                   topk_w, miss_count, miss_token, miss_expert, miss_weight, ws, MOE_STATIC_WORKSPACE_BYTES, stream);
 }
 
 int moe_quantize_mx_e4m3(const void* in, int in_dtype, int rows, int K, uint8_t* codes, uint8_t* scales,

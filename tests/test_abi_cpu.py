@@ -264,3 +264,17 @@ def test_ffn_workspace_layout(L):
             assert off_a + R * I * (4 if f in (0, 2) else 2) <= size
     with pytest.raises(moe.MoeError):
         moe.moe_expert_ffn_workspace_layout(w("fp8", 384), T, k, 9, A)
+
+
+def test_static_layer_rejects_oversize_calls(L):
+    """moe_layer_static checks the call's workspace need against its static workspace on the host,
+    before any HIP call: a 4096-token batch is refused with a message naming both sizes."""
+    w = moe.weights("fp8", 384, 4096, 1024, FAKE, FAKE, FAKE, FAKE)
+    cfg = moe.routing(384, 8, "sigmoid", True)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_static(FAKE, moe.MOE_BF16, 4096, None, FAKE, None, cfg, None, w, moe.MOE_PATH_AUTO,
+                             moe.MOE_MODE_A, FAKE, moe.MOE_BF16, FAKE, FAKE, None, None, None, None, 0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED and "static" in str(ei.value)
+    need = moe.moe_layer_workspace_size(192, cfg, w, moe.MOE_PATH_AUTO, moe.MOE_MODE_A, 0)
+    assert need <= moe.MOE_STATIC_WORKSPACE_BYTES < moe.moe_layer_workspace_size(200, cfg, w, moe.MOE_PATH_AUTO,
+                                                                                 moe.MOE_MODE_A, 0)

@@ -66,11 +66,51 @@ def build(jobs: int = 8, verbose: bool = False, extra=(), out: str = LIB, build_
     return out
 
 
+# The host-side argument checking and workspace carving of the C ABI (moe_abi.cpp) built with the
+# address and undefined-behaviour sanitizers on its host code only, linked with the ordinary
+# objects of every other source into a second library for the CPU tests.  Loading it needs the
+# sanitizer runtime preloaded (sanitizer_runtime()).
+SAN_LIB = os.path.join(PKG, "libmoe_hip_san.so")
+SAN_FLAGS = ["-g", "-O1", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """The clang address-sanitizer runtime (it carries the undefined-behaviour runtime too)."""
+    import glob
+    cands = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not cands:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/lib/llvm")
+    return cands[-1]
+
+
+def build_sanitized_abi(jobs: int = 8, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    san_dir = os.path.join(BUILD, "san")
+    os.makedirs(san_dir, exist_ok=True)
+    others = [src for src in SOURCES if src != "moe_abi.cpp"]
+    with ThreadPoolExecutor(max(1, jobs)) as ex:
+        objs = list(ex.map(lambda s_: _compile(s_, BUILD), others))
+    objs.append(_compile("moe_abi.cpp", san_dir, SAN_FLAGS))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    ap.add_argument("--sanitized-abi", action="store_true", help="also build libmoe_hip_san.so")
     a = ap.parse_args(argv)
     build(a.jobs, verbose=True)
+    if a.sanitized_abi:
+        build_sanitized_abi(a.jobs, verbose=True)
     return 0
 
 

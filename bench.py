@@ -51,8 +51,11 @@ GATE_UP_SOURCES = {
     "gemv": ["routed_expert_ffn_05_amd/csrc/gemv_impl.h", "routed_expert_ffn_05_amd/csrc/common.h"],
     "gemm": ["routed_expert_ffn_05_amd/csrc/gemm.hip", "routed_expert_ffn_05_amd/csrc/common.h"],
     "gemm_q": ["routed_expert_ffn_05_amd/csrc/gemm.hip", "routed_expert_ffn_05_amd/csrc/common.h"],
+    "decode": ["routed_expert_ffn_05_amd/csrc/gemv_impl.h", "routed_expert_ffn_05_amd/csrc/common.h",
+               "routed_expert_ffn_05_amd/csrc/topk.h"],
 }
-GATE_UP_KERNELS = {"gemv": "gemv::gate_up_kernel", "gemm": "gemm::gemm_kernel", "gemm_q": "gemm::gemm_q_kernel"}
+GATE_UP_KERNELS = {"gemv": "gemv::gate_up_kernel", "gemm": "gemm::gemm_kernel", "gemm_q": "gemm::gemm_q_kernel",
+                   "decode": "gemv::decode_gate_up_kernel"}
 
 
 def log(*a):
@@ -489,6 +492,14 @@ def run(args):
         pws_b = D.workspace(pb_bytes)
         fb_bytes = moe.moe_expert_ffn_workspace_size(desc_b, T, k, path, mode)
         fws_b = D.workspace(fb_bytes)
+    # small decode batches: moe_layer's two-launch flow (routing + gate/up, down + combine), after
+    # the router logits when router weights are given -- the same calls moe_layer makes
+    fused = not (tiers or lru) and moe.moe_layer_decode_fused(T, rcfg, desc, path, mode, xdt)
+    if fused:
+        row_slot = torch.empty(R, dtype=torch.int32, device=dev)
+        a_dec = torch.empty((R, I), dtype=torch.float32, device=dev)
+        err_w = D.workspace(256)
+        lbuf = torch.empty((T, E), dtype=torch.float32, device=dev) if d_wr is not None else None
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
@@ -496,6 +507,20 @@ def run(args):
         # with the LRU every call takes the next batch of the stream, so that no batch comes back
         r = (lru_step[0] if lru else i) % len(rot)
         dsc = descs[i % ncopy] if dsc is None else dsc
+        if fused:
+            lg = d_lg[r]
+            if d_wr is not None:
+                moe.moe_route(d_x[r], xdt, T, H, d_wr, None, None, rcfg, None, None, lbuf, None, 0, sp)
+                lg = lbuf
+            if ev is not None:
+                ev[0].record(stream)
+            moe.moe_decode_gate_up(d_x[r], xdt, T, lg, None, rcfg, d_sm, dsc, topk_idx, topk_w, row_slot, a_dec,
+                                   mc, mt if compact else None, me if compact else None, mw if compact else None,
+                                   err_w, sp)
+            if ev is not None:
+                ev[1].record(stream)
+            moe.moe_decode_down_combine(dsc, T, rcfg, row_slot, topk_w, a_dec, out, odt, sp)
+            return
         moe.moe_route_permute(d_x[r], xdt, T, H, d_wr, d_lg[r], None, rcfg, d_sm, S, topk_idx, topk_w, counts,
                               off, perm, inv, mc if compact else None, mt if compact else None,
                               me if compact else None, mw if compact else None, pws, rp_bytes, sp)
@@ -521,7 +546,7 @@ def run(args):
     for r in range(len(rot)):
         step(r)
         torch.cuda.synchronize()
-        cnt = counts.cpu().numpy()
+        cnt = np.bincount(topk_idx.cpu().numpy().reshape(-1), minlength=E)[:E] if fused else counts.cpu().numpy()
         if slot_map is not None:
             res = slot_map >= 0
             touched = int(((cnt > 0) & res).sum())
@@ -540,7 +565,10 @@ def run(args):
 
     def gate_up_bytes(r):
         touched, n_res, _ = per_rot[r]
-        return touched * slot_bytes_gu + T * H * xb + n_res * I * (2 if gemm else 4)
+        b = touched * slot_bytes_gu + T * H * xb + n_res * I * (2 if gemm else 4)
+        if fused:  # the launch also reads the logits (and the slot map) to route the batch itself
+            b += T * E * 4 + (E * 4 if compact else 0)
+        return b
 
     def gate_up_flops(r):
         return per_rot[r][1] * 2.0 * H * 2 * I
@@ -588,7 +616,7 @@ def run(args):
         f"{', '.join(f'{b * 1e3 / args.steps:.1f}' for b in block_ms)}; host enqueue {host * 1e6 / args.steps:.1f} us/step, "
         f"wall {wall * 1e6 / args.steps:.1f} us/step), "
         f"gate/up {np.mean(gu_ms) * 1e3:.1f} us avg, {achieved:.0f} GB/s; layer {layer_gbs:.0f} GB/s; "
-        f"path {'gemm' if gemm else 'gemv'}; {ncopy} weight copies")
+        f"path {'gemm' if gemm else 'gemv'}{' (two-launch decode layer)' if fused else ''}; {ncopy} weight copies")
 
     lru_share = None
     if lru:
@@ -645,7 +673,7 @@ def run(args):
     for flag in ("plan_slots", "lru", "tiers"):
         if getattr(args, flag):
             key += "_" + flag
-    kind = ("gemm_q" if mode == moe.MOE_MODE_B else "gemm") if gemm else "gemv"
+    kind = ("gemm_q" if mode == moe.MOE_MODE_B else "gemm") if gemm else "decode" if fused else "gemv"
     traffic = recorded_traffic(kind, key)
     tflops = sum(gate_up_flops(i % len(rot)) for i in step_ids) / (sum(gu_ms) / 1e3) / 1e12
     # the whole expert FFN (gate/up + down) of the median block: algorithmic flops over the step
@@ -654,7 +682,8 @@ def run(args):
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": (("moe::gemm::gemm_q_kernel" if mode == moe.MOE_MODE_B else "moe::gemm::gemm_kernel")
-                           + " (gate/up)") if gemm else "moe::gemv::gate_up_kernel",
+                           + " (gate/up)") if gemm else
+                          "moe::gemv::decode_gate_up_kernel (routing + gate/up)" if fused else "moe::gemv::gate_up_kernel",
                 "bytes_per_launch": round(sum(gu_bytes) / len(gu_bytes)),
                 "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2)}
     if traffic is not None:
@@ -714,7 +743,9 @@ def run(args):
                                 else "seeded" if slot_map is not None else "all resident"),
                    "timing": (f"HIP graph of {graph['layers']} layers ({graph['weight_copies']} weight copies), "
                               f"per-layer time of its replays" if graph else
-                              f"eager launches; median of {R} blocks of {args.steps} steps; gate/up timed by fence-free HIP events")},
+                              f"eager launches; median of {R} blocks of {args.steps} steps; gate/up timed by fence-free HIP events"),
+                   "flow": ("two-launch decode layer (routing + gate/up; down + combine)" if fused else
+                            "staged launches (route + permute, gate/up, down, combine)")},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

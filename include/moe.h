@@ -132,7 +132,8 @@ typedef struct moe_routing {
  *   topk_idx  device int32 [T, k] out: expert ids, descending logit, ties to the smaller id
  *   topk_w    device fp32 [T, k] out: gates (renormalised if cfg->renorm)
  *   logits_out device fp32 [T, E] out or NULL: with w_router, where the computed logits (+bias)
- *             are stored; NULL keeps them in the workspace
+ *             are stored; NULL keeps them in the workspace.  With w_router and logits_out given,
+ *             topk_idx and topk_w may both be NULL: then only the logits are computed (one launch)
  *   ws        device workspace of moe_route_workspace_size() bytes (may be 0 bytes / NULL)
  * ------------------------------------------------------------------------------------------ */
 size_t moe_route_workspace_size(int T, const moe_routing* cfg, int with_router_weights);
@@ -266,6 +267,55 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
               int32_t* topk_idx, float* topk_w, int32_t* miss_count, int32_t* miss_token,
               int32_t* miss_expert, float* miss_weight, void* ws, size_t ws_bytes,
               void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_layer_decode_fused -- whether moe_layer runs this batch as the two-launch decode layer.
+ * It does for T <= 4 tokens and T*k <= 16 rows on the GEMV path (`path` resolved as
+ * moe_resolve_path does) in mode A, when the two launches' LDS fits: T rows of x plus the E-entry
+ * slot map within 96 KB, and T*k fp32 rows of a plus their output columns within 144 KB.  There
+ * every work-group of the first launch selects the batch's experts itself from the logits (a
+ * wave per token; the router logits of w_router are computed first, by their own launch) and
+ * computes gate/up for one resident slot, and the second launch computes the down projection of
+ * every row for 16 output columns and combines them in place.  The outputs (out, top-k ids and
+ * gates, miss list and count, the device error word) are the same bits as the staged launches
+ * give, since each element is formed by the same arithmetic in the same order; only fewer
+ * launches and fewer dependent memory round trips separate a decode layer's inputs from its
+ * output (the pages' decode step: MoET hybrid table, row "the step").
+ * Returns 1 or 0, or -1 for invalid arguments.
+ * ------------------------------------------------------------------------------------------ */
+int moe_layer_decode_fused(int T, const moe_routing* cfg, const moe_weights* w, int path, int mode,
+                           int x_dtype);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_decode_gate_up, moe_decode_down_combine -- the two launches of the decode layer, for
+ * callers that schedule them themselves (moe_layer makes exactly these calls, after the router
+ * logits when router weights are given).  Shapes as moe_layer_decode_fused requires (T <= 4,
+ * T*k <= 16, the LDS rule); MOE_ERR_UNSUPPORTED otherwise.  Call them in order on one stream.
+ *
+ * moe_decode_gate_up: routing (top-k of the given logits, scores and gates as moe_route), the
+ * slot of each row, the compact miss list (as moe_permute) and a = silu(x W_g^T) * (x W_u^T) of
+ * every resident row, stored by row index (not permuted).
+ *   x            device [T, H] of x_dtype; logits device fp32 [T, E]; bias device fp32 [E] or NULL
+ *   slot_map     device int32 [E] or NULL (then w->S == cfg->E)
+ *   topk_idx, topk_w  device [T, k] out
+ *   row_slot     device int32 [T*k] out: slot of row t*k+j, -1 when it has none here
+ *   a            device fp32 [T*k, I] out (16-byte aligned); rows without a slot are not written
+ *   miss_count   device int32 [1] out; miss_token / miss_expert / miss_weight device [T*k] out
+ *                (required with slot_map, ignored without)
+ *   err          device uint32 word out: 1 when a slot_map entry is outside [-1, S), else 0
+ *                (moe_check_device_error reads it)
+ * moe_decode_down_combine: out[t] = sum over j ascending of topk_w[t,j] * (a_r W_d^T) for the
+ * rows r = t*k+j with row_slot[r] >= 0, fp32, one rounding to out_dtype.
+ *   row_slot, topk_w, a  as the first call wrote them; out device [T, H] of out_dtype
+ * ------------------------------------------------------------------------------------------ */
+int moe_decode_gate_up(const void* x, int x_dtype, int T, const float* logits, const float* bias,
+                       const moe_routing* cfg, const int32_t* slot_map, const moe_weights* w,
+                       int32_t* topk_idx, float* topk_w, int32_t* row_slot, float* a,
+                       int32_t* miss_count, int32_t* miss_token, int32_t* miss_expert,
+                       float* miss_weight, uint32_t* err, void* stream);
+int moe_decode_down_combine(const moe_weights* w, int T, const moe_routing* cfg,
+                            const int32_t* row_slot, const float* topk_w, const float* a, void* out,
+                            int out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * moe_layer_static -- moe_layer for callers that cannot allocate device memory (code under HIP

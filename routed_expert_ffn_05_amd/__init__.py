@@ -76,6 +76,9 @@ _SIGS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),
     "moe_resolve_path": (_I, [_W, _I, _I, _I, _I]),
+    "moe_layer_decode_fused": (_I, [_I, _R, _W, _I, _I, _I]),
+    "moe_decode_gate_up": (_I, [_P, _I, _I, _P, _P, _R, _P, _W, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_decode_down_combine": (_I, [_W, _I, _R, _P, _P, _P, _P, _I, _P]),
 }
 
 _lib = None
@@ -202,6 +205,28 @@ def moe_expert_ffn_workspace_layout(w, T, k, path, mode):
 
 def moe_resolve_path(w, T, k, path, mode) -> int:
     return lib().moe_resolve_path(_ref(w), T, k, path, mode)
+
+
+def moe_decode_gate_up(x, x_dtype, T, logits, bias, cfg, slot_map, w, topk_idx, topk_w, row_slot, a, miss_count,
+                       miss_token, miss_expert, miss_weight, err, stream=None):
+    _check(lib().moe_decode_gate_up(_ptr(x), x_dtype, T, _ptr(logits), _ptr(bias), _ref(cfg), _ptr(slot_map),
+                                    _ref(w), _ptr(topk_idx), _ptr(topk_w), _ptr(row_slot), _ptr(a),
+                                    _ptr(miss_count), _ptr(miss_token), _ptr(miss_expert), _ptr(miss_weight),
+                                    _ptr(err), _stream(stream)), "moe_decode_gate_up")
+
+
+def moe_decode_down_combine(w, T, cfg, row_slot, topk_w, a, out, out_dtype, stream=None):
+    _check(lib().moe_decode_down_combine(_ref(w), T, _ref(cfg), _ptr(row_slot), _ptr(topk_w), _ptr(a), _ptr(out),
+                                         out_dtype, _stream(stream)), "moe_decode_down_combine")
+
+
+def moe_layer_decode_fused(T, cfg, w, path, mode, x_dtype) -> bool:
+    """Whether moe_layer runs this batch as the two-launch decode layer (same results as the
+    staged launches)."""
+    r = lib().moe_layer_decode_fused(T, _ref(cfg), _ref(w), path, mode, x_dtype)
+    if r < 0:
+        raise MoeError(MOE_ERR_INVALID_ARG, "moe_layer_decode_fused", lib().moe_last_error().decode())
+    return bool(r)
 
 
 def moe_expert_ffn(w, x, x_dtype, T, k, perm, slot_offsets, path, mode, y_perm, ws, ws_bytes,

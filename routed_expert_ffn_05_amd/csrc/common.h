@@ -28,9 +28,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // E8M0 scale code -> fp32 value 2^(c-127) (c = 0 gives the subnormal 2^-127, 255 NaN)
 __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
   c &= 0xFFu;
-  if (c == 0) return __uint_as_float(0x00400000u);
-  if (c == 255) return __uint_as_float(0x7FC00000u);
-  return __uint_as_float(c << 23);
+  return __uint_as_float(c == 0 ? 0x00400000u : c == 255 ? 0x7FC00000u : (c << 23));
 }
 
 // two OCP e4m3fn codes (bytes 0,1 or 2,3 of w) -> fp32 (gfx950 converts the OCP format)
@@ -55,6 +53,33 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// direct LDS loads
+// ---------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) const void lds_void;
+
+// 16 bytes per lane from `src` into LDS at byte address lds + 16*lane (lds wave-uniform).
+// Written as inline assembly so that the compiler's wait insertion does not treat it as aliasing
+// every LDS read: the kernel orders these loads itself (explicit vmcnt waits and barriers), and no
+// other vector memory load is in flight while they are.  The memory clobber keeps LDS reads from
+// moving across it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(uint32_t(size_t((lds_void*)p)));
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0), expcnt unconstrained (gfx9 encoding).  lgkmcnt(0) makes this
+// wave's LDS reads of earlier steps complete before the barrier that lets a stage be reloaded.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

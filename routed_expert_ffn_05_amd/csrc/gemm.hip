@@ -46,7 +46,6 @@ constexpr int kMaxFp4Kb = 128;  // MXFP4: E8M0 scales per row staged in LDS (K <
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) const void lds_void;
 
 // K step, operand bytes per row and step, direct loads per wave and step, LDS for the stages.
 // The K step makes every weight row segment a whole 128-byte line where LDS allows (bf16: 64,
@@ -67,19 +66,6 @@ template <int WD> struct BFmt {
   static constexpr int nstage(int ns) { return BUDGET / stage_bytes(ns) < 8 ? BUDGET / stage_bytes(ns) : 8; }
 };
 
-// 16 bytes per lane from `src` into LDS at byte address lds + 16*lane (lds wave-uniform).
-// Written as inline assembly so that the compiler's wait insertion does not treat it as aliasing
-// every LDS read: the kernel orders these loads itself (explicit vmcnt waits and barriers), and no
-// other vector memory load is in flight while they are.  The memory clobber keeps LDS reads from
-// moving across it.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m), "v"(src) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(uint32_t(size_t((lds_void*)p)));
-}
 
 // swizzled position of 16-byte granule g in row r of a 256-byte tile row (16 granules)
 __device__ __forceinline__ int swz256(int r, int g) { return g ^ (r & 15); }
@@ -90,13 +76,6 @@ __device__ __forceinline__ int swz64(int r, int g) { return g ^ ((r >> 2) & 3); 
 // 32-byte rows (fp4)
 __device__ __forceinline__ int swz32(int r, int g) { return g ^ ((r >> 3) & 1); }
 
-// s_waitcnt vmcnt(n) lgkmcnt(0), expcnt unconstrained (gfx9 encoding).  lgkmcnt(0) makes this
-// wave's LDS reads of earlier steps complete before the barrier that lets a stage be reloaded.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
-}
 
 template <int WD>
 __host__ __device__ constexpr size_t row_bytes(int K) {

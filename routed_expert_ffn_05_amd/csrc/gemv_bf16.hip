@@ -10,4 +10,13 @@ hipError_t launch_gemv_gate_up_bf16(const GemvArgs& g, hipStream_t st) {
 
 hipError_t launch_gemv_down_bf16(const GemvArgs& g, hipStream_t st) { return gemv::down_dispatch<DT_BF16>(g, st); }
 
+hipError_t launch_decode_gate_up_bf16(const DecodeArgs& d, hipStream_t st) {
+  return d.xdt == DT_F32 ? gemv::decode_gate_up_dispatch<DT_BF16, DT_F32>(d, st)
+                         : gemv::decode_gate_up_dispatch<DT_BF16, DT_BF16>(d, st);
+}
+
+hipError_t launch_decode_down_combine_bf16(const DecodeArgs& d, hipStream_t st) {
+  return gemv::decode_down_dispatch<DT_BF16>(d, st);
+}
+
 }  // namespace moe

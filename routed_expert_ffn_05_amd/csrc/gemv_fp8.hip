@@ -10,4 +10,13 @@ hipError_t launch_gemv_gate_up_fp8(const GemvArgs& g, hipStream_t st) {
 
 hipError_t launch_gemv_down_fp8(const GemvArgs& g, hipStream_t st) { return gemv::down_dispatch<DT_FP8>(g, st); }
 
+hipError_t launch_decode_gate_up_fp8(const DecodeArgs& d, hipStream_t st) {
+  return d.xdt == DT_F32 ? gemv::decode_gate_up_dispatch<DT_FP8, DT_F32>(d, st)
+                         : gemv::decode_gate_up_dispatch<DT_FP8, DT_BF16>(d, st);
+}
+
+hipError_t launch_decode_down_combine_fp8(const DecodeArgs& d, hipStream_t st) {
+  return gemv::decode_down_dispatch<DT_FP8>(d, st);
+}
+
 }  // namespace moe

@@ -20,6 +20,7 @@
 #pragma once
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 #ifndef MOE_GEMV_WD
 #error "define MOE_GEMV_WD before including gemv_impl.h"
@@ -110,18 +111,88 @@ __device__ __forceinline__ void decode(const uint4 q, float scale, float* w) {
   }
 }
 
-// per-chunk scale of row n, chunk c: FP8 block scale (multiplies the chunk's partial sum) or the
-// MXFP4 E8M0 block scale (enters the conversion)
+// The chunk's weights as bf16 pairs (pair p holds elements 2p, 2p+1): exact for bf16, e4m3 and
+// e2m1 times a power-of-two scale (the conversion applies the MXFP4 scale; the FP8 block scale
+// multiplies the chunk's partial sum later).
 template <int WD>
-__device__ __forceinline__ float chunk_scale(const void* s, int n, int c, int K) {
+__device__ __forceinline__ void decode_pairs(const uint4 q, float scale, uint32_t* wp) {
+  const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+  if constexpr (WD == DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wp[i] = u[i];
+  } else if constexpr (WD == DT_FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wp[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[i], 1.0f, false));
+      wp[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[i], 1.0f, true));
+    }
+  } else if constexpr (WD == DT_MXFP4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wp[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u[i], scale, 0));
+      wp[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u[i], scale, 1));
+      wp[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u[i], scale, 2));
+      wp[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u[i], scale, 3));
+    }
+  }
+}
+
+// A chunk's partial dot product in a fixed association: element e (pair p) goes to partial sum
+// e % 4 (p % 4), and the result is (s0 + s1) + (s2 + s3).  Four independent chains instead of
+// one keep the FMA pipeline busy; every GEMV launch forms its sums this way, so the decode flows
+// give the same bits.  dot_pairs multiplies bf16 pairs with v_dot2 (both products exact in fp32).
+template <int EPC>
+__device__ __forceinline__ float dot_f32(const float* w, const float* x) {
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPC; e += 4) {
+    s0 = fmaf(w[e], x[e], s0);
+    s1 = fmaf(w[e + 1], x[e + 1], s1);
+    s2 = fmaf(w[e + 2], x[e + 2], s2);
+    s3 = fmaf(w[e + 3], x[e + 3], s3);
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int NP>
+__device__ __forceinline__ float dot_pairs(const uint32_t* w, const uint32_t* x) {
+  static_assert(NP % 4 == 0, "pairs");
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int p = 0; p < NP; p += 4) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[p]), __builtin_bit_cast(bf16x2_t, x[p]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[p + 1]), __builtin_bit_cast(bf16x2_t, x[p + 1]), s1, false);
+    s2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[p + 2]), __builtin_bit_cast(bf16x2_t, x[p + 2]), s2, false);
+    s3 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[p + 3]), __builtin_bit_cast(bf16x2_t, x[p + 3]), s3, false);
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+// bf16 inputs meet bf16-convertible weights (bf16, FP8, MXFP4) on v_dot2; anything with an fp32
+// operand on fmaf
+template <int WD, int XT>
+__host__ __device__ constexpr bool packed_dot() { return XT == DT_BF16 && WD != DT_F32; }
+
+// Per-chunk scale of row n, chunk c, in two halves: chunk_scale_bits loads the stored bits (the
+// FP8 block scale's fp32 bits, or the MXFP4 E8M0 byte), scale_of turns them into the value (the
+// factor of the chunk's FP8 partial sum, or the MXFP4 scale the conversion applies).  Keeping the
+// conversion out of the load phase lets every load of a row step be in flight before the first
+// is consumed.
+template <int WD>
+__device__ __forceinline__ uint32_t chunk_scale_bits(const void* s, int n, int c, int K) {
   if constexpr (WD == DT_FP8) {
     const int KB = (K + 127) >> 7;
-    return static_cast<const float*>(s)[size_t(n >> 7) * KB + (c >> 3)];
+    return static_cast<const uint32_t*>(s)[size_t(n >> 7) * KB + (c >> 3)];
   } else if constexpr (WD == DT_MXFP4) {
-    return e8m0_to_f32(static_cast<const uint8_t*>(s)[size_t(n) * (K >> 5) + c]);
+    return static_cast<const uint8_t*>(s)[size_t(n) * (K >> 5) + c];
   } else {
-    return 1.0f;
+    return 0u;
   }
+}
+template <int WD>
+__device__ __forceinline__ float scale_of(uint32_t bits) {
+  if constexpr (WD == DT_FP8) return __uint_as_float(bits);
+  else if constexpr (WD == DT_MXFP4) return e8m0_to_f32(bits);
+  else return 1.0f;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -132,6 +203,7 @@ __device__ __forceinline__ float chunk_scale(const void* s, int n, int c, int K)
 // ---------------------------------------------------------------------------------------------
 template <int XT, int EPC, int CPL>
 struct RegIn {
+  static constexpr int kXT = XT;
   static constexpr int PK = XT == DT_BF16 ? 2 : 1;
   static constexpr int WPC = EPC / PK;  // 32-bit words per chunk
   uint32_t w[CPL * WPC];
@@ -160,6 +232,11 @@ struct RegIn {
       }
     }
   }
+  // bf16 inputs as packed pairs (EPC / 2 words)
+  __device__ __forceinline__ void words(int /*t*/, int j, int /*c*/, uint32_t* xw) const {
+#pragma unroll
+    for (int e = 0; e < EPC / 2; ++e) xw[e] = w[j * WPC + e];
+  }
   __device__ __forceinline__ void chunk(int /*t*/, int j, int /*c*/, float* xv) const {
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
@@ -175,8 +252,21 @@ struct RegIn {
 
 template <int XT, int EPC>
 struct LdsIn {
+  static constexpr int kXT = XT;
   const uint8_t* base;  // token t's row at base + t * stride
   size_t stride;
+  // bf16 inputs as packed pairs (EPC / 2 words; EPC >= 8)
+  __device__ __forceinline__ void words(int t, int /*j*/, int c, uint32_t* xw) const {
+    const uint8_t* row = base + size_t(t) * stride;
+#pragma unroll
+    for (int q = 0; q < EPC / 8; ++q) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + size_t(c) * EPC * 2 + 16 * q);
+      xw[4 * q + 0] = u.x;
+      xw[4 * q + 1] = u.y;
+      xw[4 * q + 2] = u.z;
+      xw[4 * q + 3] = u.w;
+    }
+  }
   __device__ __forceinline__ void chunk(int t, int /*j*/, int c, float* xv) const {
     const uint8_t* row = base + size_t(t) * stride;
     if constexpr (XT == DT_BF16) {
@@ -225,7 +315,7 @@ __device__ __forceinline__ void dot_rows(const uint8_t* __restrict__ w, const vo
   const int CPR = K / EPC;
   const size_t rb = row_bytes<WD>(K);
   uint4 q[ROWS][CPL];
-  float sc[ROWS][CPL];
+  uint32_t sb[ROWS][CPL];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const uint4* p = reinterpret_cast<const uint4*>(w + size_t(n[r]) * rb);
@@ -234,46 +324,71 @@ __device__ __forceinline__ void dot_rows(const uint8_t* __restrict__ w, const vo
       const int c = sl + LPR * j;
       const bool ok = v[r] && c < CPR;
       q[r][j] = ok ? ld_weight16(p + c) : make_uint4(0, 0, 0, 0);
-      sc[r][j] = ok ? chunk_scale<WD>(s, n[r], c, K) : 0.0f;
+      sb[r][j] = ok ? chunk_scale_bits<WD>(s, n[r], c, K) : 0u;
     }
   }
+  // scale values only now (an invalid chunk has zero codes and a zero FP8 scale: adds nothing)
+  float sc[ROWS][CPL];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) sc[r][j] = scale_of<WD>(sb[r][j]);
+  constexpr bool kPacked = packed_dot<WD, In::kXT>();
+  auto add = [&](float& a, float d, float scale) {
+    if constexpr (WD == DT_FP8)
+      a = fmaf(scale, d, a);
+    else
+      a += d;
+  };
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = sl + LPR * j;
     if (c >= CPR) continue;
     if constexpr (NT == 1) {  // one input row: decode and consume row by row
-      float xv[EPC];
-      x.chunk(0, j, c, xv);
+      if constexpr (kPacked) {
+        uint32_t xw[EPC / 2];
+        x.words(0, j, c, xw);
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float wv[EPC];
-        decode<WD>(q[r][j], sc[r][j], wv);
-        float d = 0.0f;
+        for (int r = 0; r < ROWS; ++r) {
+          uint32_t wp[EPC / 2];
+          decode_pairs<WD>(q[r][j], sc[r][j], wp);
+          add(acc[r][0], dot_pairs<EPC / 2>(wp, xw), sc[r][j]);
+        }
+      } else {
+        float xv[EPC];
+        x.chunk(0, j, c, xv);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) d = fmaf(wv[e], xv[e], d);
-        if constexpr (WD == DT_FP8)
-          acc[r][0] = fmaf(sc[r][j], d, acc[r][0]);
-        else
-          acc[r][0] += d;
+        for (int r = 0; r < ROWS; ++r) {
+          float wv[EPC];
+          decode<WD>(q[r][j], sc[r][j], wv);
+          add(acc[r][0], dot_f32<EPC>(wv, xv), sc[r][j]);
+        }
       }
     } else {  // several input rows: decode each weight chunk once, use it for every row
-      float wv[ROWS][EPC];
+      if constexpr (kPacked) {
+        uint32_t wp[ROWS][EPC / 2];
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) decode<WD>(q[r][j], sc[r][j], wv[r]);
+        for (int r = 0; r < ROWS; ++r) decode_pairs<WD>(q[r][j], sc[r][j], wp[r]);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t < nt) {
-          float xv[EPC];
-          x.chunk(t, j, c, xv);
+        for (int t = 0; t < NT; ++t) {
+          if (t < nt) {
+            uint32_t xw[EPC / 2];
+            x.words(t, j, c, xw);
 #pragma unroll
-          for (int r = 0; r < ROWS; ++r) {
-            float d = 0.0f;
+            for (int r = 0; r < ROWS; ++r) add(acc[r][t], dot_pairs<EPC / 2>(wp[r], xw), sc[r][j]);
+          }
+        }
+      } else {
+        float wv[ROWS][EPC];
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) d = fmaf(wv[r][e], xv[e], d);
-            if constexpr (WD == DT_FP8)
-              acc[r][t] = fmaf(sc[r][j], d, acc[r][t]);
-            else
-              acc[r][t] += d;
+        for (int r = 0; r < ROWS; ++r) decode<WD>(q[r][j], sc[r][j], wv[r]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t < nt) {
+            float xv[EPC];
+            x.chunk(t, j, c, xv);
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) add(acc[r][t], dot_f32<EPC>(wv[r], xv), sc[r][j]);
           }
         }
       }
@@ -505,6 +620,415 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// Fused decode layer: T <= kDecMaxT tokens, T*k <= kDecMaxR rows, two launches.
+//
+// decode_gate_up_kernel: every work-group selects the top-k of all T tokens itself (wave t takes
+//   token t, from the logits) and maps the experts to slots; it owns one (gate, up) row pair per
+//   lane group and computes a = silu(g) * u of those pairs for every resident slot's rows (stored
+//   by row index r = t*k + j), NSL slots' weight loads in flight together.  The token rows (direct
+//   LDS loads) and the slot map are loaded while the logits are, so the weights follow after one
+//   round trip.  Work-group 0 also writes the routing outputs: top-k ids and gates, the slot of
+//   each row (-1 when the row has none) for the second launch, the compact miss list (rows in
+//   ascending r), the miss count and the error word.
+// decode_down_combine_kernel: a work-group owns RB consecutive output columns for every row: it
+//   loads all rows of a into LDS (direct LDS loads, in flight with the row slots), computes y for
+//   each resident slot's rows, NSL slots' weight loads in flight together, keeps y in LDS and
+//   sums out[t] = sum_j w[t,j] * y[t*k+j] over the computed rows in ascending j.
+//
+// Every element is formed as on the GEMV path (same lanes per row and chunks per lane, so the
+// same partial sums in the same order and the same segmented reduction; the same combine order),
+// so a token's output is the same bits whichever flow computed it.
+// ---------------------------------------------------------------------------------------------
+// The decode layer's slots are dealt to kDecGroups groups of waves (work-groups of the gate/up
+// launch, wave halves of a down + combine work-group), so each wave forms fewer slots' sums.
+constexpr int kDecGroups = 2;
+constexpr int kDecThreads2 = kThreads * kDecGroups;  // down + combine work-group
+
+// the leaders (first rows of their slots) whose index among all leaders is g mod kDecGroups
+__device__ __forceinline__ unsigned long long leaders_of_group(unsigned long long all, int g) {
+  unsigned long long mine = 0;
+  int idx = 0;
+  for (unsigned long long m = all; m; m &= m - 1, ++idx)
+    if (idx % kDecGroups == g) mine |= m & (~m + 1ull);
+  return mine;
+}
+
+// gate/up of the decode layer: one (gate, up) row pair per lane group and work-group column
+// block, NSL slots' weight loads in flight together
+template <int LPR>
+__host__ __device__ constexpr int dec_gu_pairs() { return kWaves * (64 / LPR); }
+template <int CPL>
+__host__ __device__ constexpr int dec_gu_slots() { return 16 / (2 * CPL) > 0 ? 16 / (2 * CPL) : 1; }
+
+template <int WD, int XT, int LPR, int CPL, int VPL>
+__global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(const DecodeArgs d) {
+  constexpr int EPC = WFmt<WD>::EPC;
+  constexpr int GPW = 64 / LPR;
+  constexpr int NSL = dec_gu_slots<CPL>();
+  extern __shared__ __align__(16) uint8_t dl[];
+  __shared__ int s_e[kDecMaxR];
+  __shared__ float s_w[kDecMaxR];
+  const int T = d.T, k = d.k, R = T * k, H = d.H, I = d.I, S = d.S, E = d.E;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const size_t xrow = size_t(H) * (XT == DT_F32 ? 4 : 2);
+  const int ngx = T * int(xrow >> 4);                                  // 16-byte granules of the T token rows
+  uint8_t* xl = dl;                                                    // [T][xrow]
+  int32_t* smap = reinterpret_cast<int32_t*>(dl + size_t(T) * xrow);  // [E]
+  const bool first = blockIdx.x == 0 && blockIdx.y == 0;
+  const uint8_t* xg = static_cast<const uint8_t*>(d.x);
+
+  // 1. loads that do not depend on the routing, in flight with the logits: the T token rows go
+  //    straight into LDS (direct loads, 1 KB per wave instruction), the slot map into registers
+  const uint32_t xbase = lds_addr(xl);
+  for (int g = wid * 64; g < ngx; g += kThreads)
+    if (g + lane < ngx) dma16(xg + size_t(g + lane) * 16, xbase + uint32_t(g) * 16);
+  constexpr int kMapPre = (1024 + kThreads - 1) / kThreads;  // E <= 1024
+  int mr[kMapPre];
+  if (d.slot_map) {
+#pragma unroll
+    for (int u = 0; u < kMapPre; ++u) {
+      const int i = tid + u * kThreads;
+      mr[u] = i < E ? d.slot_map[i] : 0;
+    }
+  }
+  // 2. token t's experts and gates in wave t
+  if (wid < T) {
+    int my_e;
+    float my_w;
+    topk_wave<VPL>(d.logits + size_t(wid) * E, d.bias, E, k, d.score, d.renorm, my_e, my_w);
+    if (lane < k) {
+      s_e[wid * k + lane] = my_e;
+      s_w[wid * k + lane] = my_w;
+      if (first) {
+        d.topk_idx[wid * k + lane] = my_e;
+        d.topk_w[wid * k + lane] = my_w;
+      }
+    }
+  }
+  if (d.slot_map) {
+#pragma unroll
+    for (int u = 0; u < kMapPre; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < E) smap[i] = mr[u];
+    }
+  }
+  wait_vmcnt<0>();  // the direct loads of the token rows
+  __syncthreads();
+
+  // 3. the slot of every row: key = slot, S for an absent expert, -1 for an out-of-range map
+  //    entry, -2 on lanes past R (each wave derives the same from LDS)
+  int key = -2, e = 0;
+  if (lane < R) {
+    e = s_e[lane];
+    const int s = d.slot_map ? smap[e] : e;
+    key = (s < -1 || s >= S) ? -1 : s < 0 ? S : s;
+  }
+  bool lead = key >= 0 && key < S;  // the first row of its slot
+  for (int q = 0; q < R; ++q) {
+    const int kq = __builtin_amdgcn_readlane(key, q);
+    if (q < lane && kq == key) lead = false;
+  }
+  const unsigned long long leaders = __ballot(lead);
+  if (first && wid == 0) {
+    const unsigned long long miss = __ballot(key == S);
+    const unsigned long long bad = __ballot(key == -1);
+    if (lane < R) d.rkey[lane] = (key >= 0 && key < S) ? key : -1;
+    if (key == S && d.miss_token) {
+      const int m = __popcll(miss & ((1ull << lane) - 1ull));
+      d.miss_token[m] = lane / k;
+      d.miss_expert[m] = e;
+      d.miss_weight[m] = s_w[lane];
+    }
+    if (lane == 0) {
+      d.miss_count[0] = __popcll(miss);
+      d.err[0] = bad ? 1u : 0u;
+    }
+  }
+  // 4. gate/up: this lane group's pair (gate row i, up row I + i) for every resident slot's rows,
+  //    each element as gate_up_kernel forms it
+  const int CPR = H / EPC;
+  const size_t rb = row_bytes<WD>(H);
+  const int grp = lane / LPR, sl = lane - grp * LPR;
+  const int i = blockIdx.x * dec_gu_pairs<LPR>() + wid * GPW + grp;
+  const bool iv = i < I;
+  const int nrow[2] = {iv ? i : 0, iv ? I + i : 0};
+  unsigned long long rest = leaders_of_group(leaders, blockIdx.y);
+  while (rest) {
+    int sv[NSL];
+    unsigned long long rm[NSL];
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      sv[u] = -1;
+      rm[u] = 0;
+      if (rest) {
+        sv[u] = __builtin_amdgcn_readlane(key, __ffsll((long long)rest) - 1);
+        rest &= rest - 1;
+        rm[u] = __ballot(key == sv[u]);
+      }
+    }
+    uint4 q[NSL][2][CPL];
+    uint32_t sb[NSL][2][CPL];
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      const int su = sv[u] < 0 ? 0 : sv[u];
+      const uint8_t* wslot = static_cast<const uint8_t*>(d.w_gu) + size_t(su) * 2 * I * rb;
+      const void* sslot = nullptr;
+      if constexpr (WD == DT_FP8)
+        sslot = static_cast<const float*>(d.s_gu) + size_t(su) * ((2 * I + 127) >> 7) * ((H + 127) >> 7);
+      if constexpr (WD == DT_MXFP4) sslot = static_cast<const uint8_t*>(d.s_gu) + size_t(su) * 2 * I * (H >> 5);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint4* p = reinterpret_cast<const uint4*>(wslot + size_t(nrow[r]) * rb);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = sl + LPR * j;
+          const bool ok = sv[u] >= 0 && iv && c < CPR;
+          q[u][r][j] = ok ? ld_weight16(p + c) : make_uint4(0, 0, 0, 0);
+          sb[u][r][j] = ok ? chunk_scale_bits<WD>(sslot, nrow[r], c, H) : 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      unsigned long long mm = rm[u];
+      while (mm) {  // the slot's rows in passes of kDecMaxT
+        int rr[kDecMaxT];
+        int ntp = 0;
+#pragma unroll
+        for (int t = 0; t < kDecMaxT; ++t) {
+          rr[t] = mm ? __ffsll((long long)mm) - 1 : 0;
+          if (mm) {
+            mm &= mm - 1;
+            ++ntp;
+          }
+        }
+        float acc[2][kDecMaxT];
+#pragma unroll
+        for (int t = 0; t < kDecMaxT; ++t) acc[0][t] = acc[1][t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = sl + LPR * j;
+          if (c >= CPR) continue;
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {  // one weight row decoded at a time
+            const float sc = scale_of<WD>(sb[u][r][j]);
+            float dd[kDecMaxT];
+            if constexpr (packed_dot<WD, XT>()) {
+              uint32_t wp[EPC / 2];
+              decode_pairs<WD>(q[u][r][j], sc, wp);
+#pragma unroll
+              for (int t = 0; t < kDecMaxT; ++t) {
+                if (t < ntp) {
+                  uint32_t xw[EPC / 2];
+                  LdsIn<XT, EPC>{xl + size_t(rr[t] / k) * xrow, 0}.words(0, 0, c, xw);
+                  dd[t] = dot_pairs<EPC / 2>(wp, xw);
+                }
+              }
+            } else {
+              float wv[EPC];
+              decode<WD>(q[u][r][j], sc, wv);
+#pragma unroll
+              for (int t = 0; t < kDecMaxT; ++t) {
+                if (t < ntp) {
+                  float xv[EPC];
+                  LdsIn<XT, EPC>{xl + size_t(rr[t] / k) * xrow, 0}.chunk(0, 0, c, xv);
+                  dd[t] = dot_f32<EPC>(wv, xv);
+                }
+              }
+            }
+#pragma unroll
+            for (int t = 0; t < kDecMaxT; ++t) {
+              if (t < ntp) {
+                if constexpr (WD == DT_FP8)
+                  acc[r][t] = fmaf(sc, dd[t], acc[r][t]);
+                else
+                  acc[r][t] += dd[t];
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < kDecMaxT; ++t) {
+          if (t < ntp) {
+            const float g = seg_sum<LPR>(acc[0][t]);
+            const float uu = seg_sum<LPR>(acc[1][t]);
+            if (sl == LPR - 1 && iv) d.a[size_t(rr[t]) * I + i] = silu(g) * uu;
+          }
+        }
+      }
+    }
+  }
+}
+
+// output rows per lane group and slot in the down + combine launch; the work-group's columns
+// RB = kWaves * (64 / LPR) * rows
+template <int LPR, int CPL, int EPC>
+__host__ __device__ constexpr int dec_rows() {
+  return LPR == 64 ? (CPL >= 16 ? 1 : (CPL >= 8 || EPC >= 32) ? 2 : 4) : LPR == 32 ? 2 : 1;
+}
+template <int LPR, int CPL, int EPC>
+__host__ __device__ constexpr int dec_cols() {
+  return kWaves * (64 / LPR) * dec_rows<LPR, CPL, EPC>();
+}
+
+template <int WD, int LPR, int CPL, int ODT>
+__global__ __launch_bounds__(kDecThreads2) void decode_down_combine_kernel(const DecodeArgs d) {
+  constexpr int EPC = WFmt<WD>::EPC;
+  constexpr int GPW = 64 / LPR;
+  constexpr int ROWS = dec_rows<LPR, CPL, EPC>();
+  constexpr int RB = dec_cols<LPR, CPL, EPC>();
+  static_assert(RB <= kDecRB, "column block");
+  constexpr int NSL = 8 / (ROWS * CPL) > 0 ? 8 / (ROWS * CPL) : 1;  // slots whose loads fly together
+  extern __shared__ __align__(16) uint8_t dl[];
+  __shared__ int s_key[kDecMaxR];
+  __shared__ float s_w[kDecMaxR];
+  const int T = d.T, k = d.k, R = T * k, H = d.H, I = d.I, S = d.S;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int grp = lane / LPR, sl = lane - grp * LPR;
+  const size_t arow = size_t(I) * 4;
+  const uint8_t* al = dl;                                           // [R][I] fp32 rows of a
+  float* yl = reinterpret_cast<float*>(dl + size_t(R) * arow);      // [R][RB]
+  const int h0 = blockIdx.x * RB;
+
+  // 1. every row of a (direct LDS loads, 1 KB per wave instruction) and the rows' slots and gates
+  const int ng = R * (I >> 2);
+  const uint32_t abase = lds_addr(al);
+  for (int c0 = wid * 64; c0 < ng; c0 += kDecThreads2)
+    if (c0 + lane < ng) dma16(reinterpret_cast<const uint8_t*>(d.a) + size_t(c0 + lane) * 16, abase + uint32_t(c0) * 16);
+  int key = -1;
+  float gw = 0.0f;
+  if (lane < R) {
+    key = d.rkey[lane];
+    gw = d.topk_w[lane];
+  }
+  wait_vmcnt<0>();
+  if (key < 0 || key >= S) key = -1;
+  if (wid == 0 && lane < R) {
+    s_key[lane] = key;
+    s_w[lane] = gw;
+  }
+  __syncthreads();
+
+  // 2. y of every resident slot's rows for this work-group's columns
+  bool lead = key >= 0;  // the first row of its slot
+  for (int q = 0; q < R; ++q) {
+    const int kq = __builtin_amdgcn_readlane(key, q);
+    if (q < lane && kq == key) lead = false;
+  }
+  // wave half g = wid / kWaves takes every kDecGroups-th slot; both halves cover the same columns
+  unsigned long long rest = leaders_of_group(__ballot(lead), wid / kWaves);
+  const int CPR = I / EPC;
+  const size_t rb = row_bytes<WD>(I);
+  const int hb = h0 + ((wid % kWaves) * GPW + grp) * ROWS;  // this lane group's first output row
+  while (rest) {
+    int sv[NSL];
+    unsigned long long rm[NSL];
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      sv[u] = -1;
+      rm[u] = 0;
+      if (rest) {
+        sv[u] = __builtin_amdgcn_readlane(key, __ffsll((long long)rest) - 1);
+        rest &= rest - 1;
+        rm[u] = __ballot(key == sv[u]);
+      }
+    }
+    uint4 q[NSL][ROWS][CPL];
+    uint32_t sb[NSL][ROWS][CPL];
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      const int su = sv[u] < 0 ? 0 : sv[u];
+      const uint8_t* wslot = static_cast<const uint8_t*>(d.w_d) + size_t(su) * H * rb;
+      const void* sslot = nullptr;
+      if constexpr (WD == DT_FP8)
+        sslot = static_cast<const float*>(d.s_d) + size_t(su) * ((H + 127) >> 7) * ((I + 127) >> 7);
+      if constexpr (WD == DT_MXFP4) sslot = static_cast<const uint8_t*>(d.s_d) + size_t(su) * H * (I >> 5);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const int n = hb + r;
+        const uint4* p = reinterpret_cast<const uint4*>(wslot + size_t(n < H ? n : 0) * rb);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = sl + LPR * j;
+          const bool ok = sv[u] >= 0 && n < H && c < CPR;
+          q[u][r][j] = ok ? ld_weight16(p + c) : make_uint4(0, 0, 0, 0);
+          sb[u][r][j] = ok ? chunk_scale_bits<WD>(sslot, n, c, I) : 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      unsigned long long mm = rm[u];
+      while (mm) {  // the slot's rows in passes of kDecMaxT
+        int rr[kDecMaxT];
+        int ntp = 0;
+#pragma unroll
+        for (int t = 0; t < kDecMaxT; ++t) {
+          rr[t] = mm ? __ffsll((long long)mm) - 1 : 0;
+          if (mm) {
+            mm &= mm - 1;
+            ++ntp;
+          }
+        }
+        float acc[ROWS][kDecMaxT];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+          for (int t = 0; t < kDecMaxT; ++t) acc[r][t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = sl + LPR * j;
+          if (c >= CPR) continue;
+#pragma unroll
+          for (int r = 0; r < ROWS; ++r) {  // one weight row decoded at a time
+            float wv[EPC];
+            const float sc = scale_of<WD>(sb[u][r][j]);
+            decode<WD>(q[u][r][j], sc, wv);
+#pragma unroll
+            for (int t = 0; t < kDecMaxT; ++t) {
+              if (t < ntp) {
+                float xv[EPC];
+                LdsIn<DT_F32, EPC>{al + size_t(rr[t]) * arow, 0}.chunk(0, 0, c, xv);
+                const float dd = dot_f32<EPC>(wv, xv);
+                if constexpr (WD == DT_FP8)
+                  acc[r][t] = fmaf(sc, dd, acc[r][t]);
+                else
+                  acc[r][t] += dd;
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+          for (int t = 0; t < kDecMaxT; ++t) {
+            if (t < ntp) {
+              const float sum = seg_sum<LPR>(acc[r][t]);
+              if (sl == LPR - 1 && hb + r < H) yl[rr[t] * RB + (hb - h0) + r] = sum;
+            }
+          }
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. combine: out[t, h] = sum over the computed rows t*k+j, j ascending, of w * y
+  for (int i = tid; i < T * RB; i += kDecThreads2) {
+    const int t = i / RB, hl = i - t * RB, h = h0 + hl;
+    if (h >= H) continue;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int r = t * k + j;
+      if (s_key[r] >= 0) acc = fmaf(s_w[r], yl[r * RB + hl], acc);
+    }
+    if constexpr (ODT == DT_F32)
+      static_cast<float*>(d.out)[size_t(t) * H + h] = acc;
+    else
+      static_cast<uint16_t*>(d.out)[size_t(t) * H + h] = f32_to_bf16(acc);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // host dispatch
 // ---------------------------------------------------------------------------------------------
 // lanes per row and chunks per lane for a row of CPR chunks
@@ -598,6 +1122,75 @@ hipError_t down_dispatch(const GemvArgs& g, hipStream_t st) {
     case 4: return launch_down_t<WD, 64, 4>(g, st);
     case 8: return launch_down_t<WD, 64, 8>(g, st);
     default: return launch_down_t<WD, 64, 16>(g, st);
+  }
+}
+
+template <int WD, int XT, int LPR, int CPL>
+hipError_t launch_decode_gate_up_t(const DecodeArgs& d, hipStream_t st) {
+  constexpr int PB = dec_gu_pairs<LPR>();
+  dim3 grid((d.I + PB - 1) / PB, kDecGroups), block(kThreads);
+  const size_t lds = size_t(d.T) * d.H * (XT == DT_F32 ? 4 : 2) + size_t(d.E) * 4;
+  const void* kern = d.E <= 512 ? (const void*)decode_gate_up_kernel<WD, XT, LPR, CPL, 8>
+                                : (const void*)decode_gate_up_kernel<WD, XT, LPR, CPL, 16>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  if (d.E <= 512)
+    decode_gate_up_kernel<WD, XT, LPR, CPL, 8><<<grid, block, lds, st>>>(d);
+  else
+    decode_gate_up_kernel<WD, XT, LPR, CPL, 16><<<grid, block, lds, st>>>(d);
+  return hipGetLastError();
+}
+
+template <int WD, int XT>
+hipError_t decode_gate_up_dispatch(const DecodeArgs& d, hipStream_t st) {
+  int lpr, cpl;
+  pick_lpr_cpl(d.H / WFmt<WD>::EPC, lpr, cpl);  // as gate_up_dispatch: the same lanes per row
+  if (lpr == 16) return launch_decode_gate_up_t<WD, XT, 16, 1>(d, st);
+  if (lpr == 32) return launch_decode_gate_up_t<WD, XT, 32, 1>(d, st);
+  switch (cpl) {
+    case 1: return launch_decode_gate_up_t<WD, XT, 64, 1>(d, st);
+    case 2: return launch_decode_gate_up_t<WD, XT, 64, 2>(d, st);
+    case 4: return launch_decode_gate_up_t<WD, XT, 64, 4>(d, st);
+    case 8: return launch_decode_gate_up_t<WD, XT, 64, 8>(d, st);
+    default: return launch_decode_gate_up_t<WD, XT, 64, 16>(d, st);
+  }
+}
+
+template <int WD, int LPR, int CPL>
+hipError_t launch_decode_down_t(const DecodeArgs& d, hipStream_t st) {
+  constexpr int RB = dec_cols<LPR, CPL, WFmt<WD>::EPC>();
+  dim3 grid((d.H + RB - 1) / RB), block(kDecThreads2);
+  const size_t R = size_t(d.T) * d.k;
+  const size_t lds = R * d.I * 4 + R * RB * 4;
+  const void* kern = d.odt == DT_F32 ? (const void*)decode_down_combine_kernel<WD, LPR, CPL, DT_F32>
+                                     : (const void*)decode_down_combine_kernel<WD, LPR, CPL, DT_BF16>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  if (d.odt == DT_F32)
+    decode_down_combine_kernel<WD, LPR, CPL, DT_F32><<<grid, block, lds, st>>>(d);
+  else
+    decode_down_combine_kernel<WD, LPR, CPL, DT_BF16><<<grid, block, lds, st>>>(d);
+  return hipGetLastError();
+}
+
+template <int WD>
+hipError_t decode_down_dispatch(const DecodeArgs& d, hipStream_t st) {
+  int lpr, cpl;
+  pick_lpr_cpl(d.I / WFmt<WD>::EPC, lpr, cpl);
+  // the same lanes per row and chunks per lane as down_dispatch
+  if (d.I / WFmt<WD>::EPC == 64) return launch_decode_down_t<WD, 16, 4>(d, st);
+  if (lpr == 16) return launch_decode_down_t<WD, 16, 1>(d, st);
+  if (lpr == 32) return launch_decode_down_t<WD, 32, 1>(d, st);
+  switch (cpl) {
+    case 1: return launch_decode_down_t<WD, 64, 1>(d, st);
+    case 2: return launch_decode_down_t<WD, 64, 2>(d, st);
+    case 4: return launch_decode_down_t<WD, 64, 4>(d, st);
+    case 8: return launch_decode_down_t<WD, 64, 8>(d, st);
+    default: return launch_decode_down_t<WD, 64, 16>(d, st);
   }
 }
 

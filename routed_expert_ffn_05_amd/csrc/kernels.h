@@ -44,6 +44,40 @@ struct GemvArgs {
 hipError_t launch_gemv_gate_up(const GemvArgs& g, hipStream_t st);
 hipError_t launch_gemv_down(const GemvArgs& g, hipStream_t st);
 
+// Fused decode layer for small batches (two launches, see gemv_impl.h): routing, permutation and
+// gate/up in the first; down projection and combine in the second.
+constexpr int kDecMaxT = 4;    // tokens: one wave of a work-group selects each token's experts
+constexpr int kDecMaxR = 64;   // rows T*k: one wave holds the slot of every row
+constexpr int kDecFuseRows = 16;  // rows T*k up to which moe_layer takes the decode layer
+constexpr int kDecRB = 16;     // output columns per work-group of the down + combine launch
+struct DecodeArgs {
+  int wdt, xdt, odt;
+  int S, T, k, H, I, E;
+  int score, renorm;
+  const float* logits;     // [T, E] router logits
+  const float* bias;       // [E] selection bias or null
+  const int32_t* slot_map; // [E] expert -> slot (-1: absent) or null (slot = expert)
+  const void* w_gu;
+  const void* s_gu;
+  const void* w_d;
+  const void* s_d;
+  const void* x;           // [T, H]
+  int32_t* topk_idx;       // [T*k] out
+  float* topk_w;           // [T*k] out
+  int32_t* rkey;           // [T*k] out: slot of row t*k+j, -1 when the row is not computed here
+  int32_t* miss_count;     // [1] out
+  int32_t* miss_token;     // [T*k] out (null without a slot map)
+  int32_t* miss_expert;
+  float* miss_weight;
+  uint32_t* err;           // [1] out: 1 when a slot_map entry is out of range
+  float* a;                // [T*k, I] fp32, by row index t*k+j
+  void* out;               // [T, H]
+};
+// whether the two-launch decode layer takes this shape (LDS budgets, row and token limits)
+bool decode_fused_fits(int T, int k, int E, int H, int I, int xdt);
+hipError_t launch_decode_gate_up(const DecodeArgs& d, hipStream_t st);
+hipError_t launch_decode_down_combine(const DecodeArgs& d, hipStream_t st);
+
 struct GemmArgs {
   int wdt, xdt;
   int S, T, k, H, I;

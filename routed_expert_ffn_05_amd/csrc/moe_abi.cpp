@@ -250,7 +250,8 @@ int moe_route(const void* x, int x_dtype, int T, int H, const float* w_router, c
   MOE_TRY(check_T(T, cfg->k));
   if ((w_router == nullptr) == (logits == nullptr))
     return fail(MOE_ERR_INVALID_ARG, "exactly one of w_router / logits must be given");
-  if (T > 0 && (!topk_idx || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_w is NULL");
+  const bool logits_only = !topk_idx && !topk_w && w_router && logits_out;
+  if (T > 0 && !logits_only && (!topk_idx || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "topk_idx / topk_w is NULL");
   if (w_router) {
     MOE_TRY(check_act_dtype(x_dtype, "x"));
     if (H < 4 || H % 4 || H > kMaxDim)
@@ -269,6 +270,7 @@ int moe_route(const void* x, int x_dtype, int T, int H, const float* w_router, c
     hipError_t e = moe::launch_router_logits(x, x_dtype, w_router, bias, lo, T, H, cfg->E, st);
     if (e != hipSuccess) return hip_fail(e, "router logits");
     l = lo;
+    if (logits_only) return MOE_OK;
   }
   hipError_t e = moe::launch_topk(l, bias, (w_router == nullptr && bias) ? 1 : 0, T, cfg->E, cfg->k,
                                   cfg->score, cfg->renorm, topk_idx, topk_w, st);
@@ -607,6 +609,95 @@ LayerWs carve_layer(void* ws, int T, const moe_routing* cfg, const moe_weights* 
 }
 }  // namespace
 
+namespace {
+int check_decode_shape(int T, const moe_routing* cfg, const moe_weights* w, int x_dtype) {
+  MOE_TRY(check_routing(cfg));
+  MOE_TRY(check_T(T, cfg->k));
+  MOE_TRY(check_weights(w));
+  MOE_TRY(check_act_dtype(x_dtype, "x"));
+  if (!moe::decode_fused_fits(T, cfg->k, cfg->E, w->H, w->I, x_dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "T = %d, k = %d, H = %d, I = %d: outside the two-launch decode layer", T, cfg->k,
+                w->H, w->I);
+  return MOE_OK;
+}
+
+moe::DecodeArgs decode_args(int T, const moe_routing* cfg, const moe_weights* w) {
+  moe::DecodeArgs d{};
+  d.wdt = w->wdtype;
+  d.S = w->S;
+  d.T = T;
+  d.k = cfg->k;
+  d.H = w->H;
+  d.I = w->I;
+  d.E = cfg->E;
+  d.score = cfg->score;
+  d.renorm = cfg->renorm;
+  d.w_gu = w->w_gu;
+  d.s_gu = w->s_gu;
+  d.w_d = w->w_d;
+  d.s_d = w->s_d;
+  return d;
+}
+}  // namespace
+
+int moe_decode_gate_up(const void* x, int x_dtype, int T, const float* logits, const float* bias,
+                       const moe_routing* cfg, const int32_t* slot_map, const moe_weights* w, int32_t* topk_idx,
+                       float* topk_w, int32_t* row_slot, float* a, int32_t* miss_count, int32_t* miss_token,
+                       int32_t* miss_expert, float* miss_weight, uint32_t* err, void* stream) {
+  MOE_TRY(check_decode_shape(T, cfg, w, x_dtype));
+  if (!slot_map && w->S != cfg->E) return fail(MOE_ERR_INVALID_ARG, "without slot_map S (%d) must equal E (%d)", w->S, cfg->E);
+  if (w->S > cfg->E) return fail(MOE_ERR_INVALID_ARG, "S = %d above E = %d", w->S, cfg->E);
+  if (!x || !logits || !topk_idx || !topk_w || !row_slot || !a || !miss_count || !err)
+    return fail(MOE_ERR_INVALID_ARG, "a NULL pointer among x, logits, topk_idx, topk_w, row_slot, a, miss_count, err");
+  if (slot_map && (!miss_token || !miss_expert || !miss_weight))
+    return fail(MOE_ERR_INVALID_ARG, "a slot_map needs miss_token, miss_expert and miss_weight");
+  if (!aligned(x, 16) || !aligned(a, 16)) return fail(MOE_ERR_INVALID_ARG, "x / a must be 16-byte aligned");
+  moe::DecodeArgs d = decode_args(T, cfg, w);
+  d.xdt = x_dtype;
+  d.logits = logits;
+  d.bias = bias;
+  d.slot_map = slot_map;
+  d.x = x;
+  d.topk_idx = topk_idx;
+  d.topk_w = topk_w;
+  d.rkey = row_slot;
+  d.miss_count = miss_count;
+  d.miss_token = slot_map ? miss_token : nullptr;
+  d.miss_expert = slot_map ? miss_expert : nullptr;
+  d.miss_weight = slot_map ? miss_weight : nullptr;
+  d.err = err;
+  d.a = a;
+  hipError_t e = moe::launch_decode_gate_up(d, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode gate/up");
+  return MOE_OK;
+}
+
+int moe_decode_down_combine(const moe_weights* w, int T, const moe_routing* cfg, const int32_t* row_slot,
+                            const float* topk_w, const float* a, void* out, int out_dtype, void* stream) {
+  MOE_TRY(check_decode_shape(T, cfg, w, MOE_BF16));
+  MOE_TRY(check_act_dtype(out_dtype, "out"));
+  if (!row_slot || !topk_w || !a || !out) return fail(MOE_ERR_INVALID_ARG, "a NULL pointer among row_slot, topk_w, a, out");
+  if (!aligned(a, 16) || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "a / out must be 16-byte aligned");
+  moe::DecodeArgs d = decode_args(T, cfg, w);
+  d.odt = out_dtype;
+  d.rkey = const_cast<int32_t*>(row_slot);
+  d.topk_w = const_cast<float*>(topk_w);
+  d.a = const_cast<float*>(a);
+  d.out = out;
+  hipError_t e = moe::launch_decode_down_combine(d, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode down + combine");
+  return MOE_OK;
+}
+
+int moe_layer_decode_fused(int T, const moe_routing* cfg, const moe_weights* w, int path, int mode,
+                           int x_dtype) {
+  if (check_routing(cfg) != MOE_OK || check_T(T, cfg->k) != MOE_OK || check_weights(w) != MOE_OK ||
+      check_path_mode(path, mode, w) != MOE_OK || check_act_dtype(x_dtype, "x") != MOE_OK)
+    return -1;
+  return resolve_path(path, T, cfg->k, w, mode) == MOE_PATH_GEMV && mode == MOE_MODE_A &&
+         moe::decode_fused_fits(T, cfg->k, cfg->E, w->H, w->I, x_dtype);
+}
+
 size_t moe_layer_workspace_size(int T, const moe_routing* cfg, const moe_weights* w, int path,
                                 int mode, int with_router_weights) {
   if (!cfg || !w || T < 0 || cfg->k < 1 || cfg->E < 1) return 0;
@@ -644,6 +735,20 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
   LayerWs L = carve_layer(ws, T, cfg, w, rp, mode, with_rw);
   int32_t* tidx = topk_idx ? topk_idx : L.topk_idx;
   float* tw = topk_w ? topk_w : L.topk_w;
+  if (T > 0 && moe_layer_decode_fused(T, cfg, w, path, mode, x_dtype) == 1) {
+    // the two-launch decode layer (after the router logits, when router weights are given)
+    uint32_t* err = static_cast<uint32_t*>(L.rp);  // the error word moe_check_device_error reads
+    float* lbuf = reinterpret_cast<float*>(static_cast<char*>(L.rp) + 256);
+    if (w_router) {
+      hipError_t e = moe::launch_router_logits(x, x_dtype, w_router, bias, lbuf, T, w->H, cfg->E, as_stream(stream));
+      if (e != hipSuccess) return hip_fail(e, "router logits");
+    }
+    float* a = static_cast<float*>(carve_ffn(L.ffn, w, T, cfg->k, mode).a);
+    MOE_TRY(moe_decode_gate_up(x, x_dtype, T, w_router ? lbuf : logits, w_router ? nullptr : bias, cfg, slot_map, w,
+                               tidx, tw, L.inv, a, miss_count ? miss_count : L.miss_count, miss_token, miss_expert,
+                               miss_weight, err, stream));
+    return moe_decode_down_combine(w, T, cfg, L.inv, tw, a, out, out_dtype, stream);
+  }
   MOE_TRY(moe_route_permute(x, x_dtype, T, w->H, w_router, logits, bias, cfg, slot_map, w->S, tidx, tw,
                             L.counts, L.offsets, L.perm, L.inv, miss_count ? miss_count : L.miss_count,
                             miss_token, miss_expert, miss_weight, L.rp, L.rp_bytes, stream));

@@ -278,3 +278,51 @@ def test_static_layer_rejects_oversize_calls(L):
     need = moe.moe_layer_workspace_size(192, cfg, w, moe.MOE_PATH_AUTO, moe.MOE_MODE_A, 0)
     assert need <= moe.MOE_STATIC_WORKSPACE_BYTES < moe.moe_layer_workspace_size(200, cfg, w, moe.MOE_PATH_AUTO,
                                                                                  moe.MOE_MODE_A, 0)
+
+
+def test_layer_decode_fused_rule(L):
+    """Which batches moe_layer runs as the two-launch decode layer."""
+    bf = moe.MOE_BF16
+    cfg = moe.routing(384, 8, "sigmoid")
+
+    def fused(T, k=8, I=1024, wd=moe.MOE_BF16, path=moe.MOE_PATH_GEMV, mode=moe.MOE_MODE_A, xdt=bf, E=384):
+        c = moe.routing(E, k, "sigmoid")
+        w = moe.weights(wd, E, 4096, I, FAKE, FAKE, FAKE, FAKE)
+        return moe.moe_layer_decode_fused(T, c, w, path, mode, xdt)
+    assert fused(1) and fused(2) and fused(4, k=4)     # up to 16 rows
+    assert not fused(4)                                # 32 rows: the staged launches
+    assert not fused(5, k=2)                           # a fifth token
+    assert not fused(1, k=64, I=512)                   # 64 rows
+    assert fused(1, k=16, I=512)
+    assert not fused(2, I=8192)                        # the rows of a beyond the LDS budget
+    assert not fused(0)
+    assert not fused(1, wd=moe.MOE_FP8_E4M3_B128, mode=moe.MOE_MODE_B)      # mode B stays staged
+    assert not fused(2, wd=moe.MOE_FP8_E4M3_B128, path=moe.MOE_PATH_GEMM)   # the matrix-core path
+    assert fused(2, wd=moe.MOE_FP8_E4M3_B128, path=moe.MOE_PATH_AUTO)        # AUTO picks the GEMV here
+    assert fused(1, xdt=moe.MOE_F32)
+    _expect(moe.MOE_ERR_INVALID_ARG, fused, 1, xdt=7)
+
+
+def test_decode_calls_validation(L):
+    """The two decode launches reject shapes outside the two-launch layer and missing buffers
+    before any HIP call."""
+    bf, inv, uns = moe.MOE_BF16, moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED
+    cfg = moe.routing(384, 8, "sigmoid")
+    w = moe.weights(moe.MOE_BF16, 384, 4096, 1024, FAKE, FAKE, FAKE, FAKE)
+    wc = moe.weights(moe.MOE_MXFP4, 110, 4096, 1024, FAKE, FAKE, FAKE, FAKE)
+
+    def gu(T=1, x=FAKE, logits=FAKE, slot_map=None, w=w, miss=FAKE, err=FAKE, a=FAKE):
+        moe.moe_decode_gate_up(x, bf, T, logits, None, cfg, slot_map, w, FAKE, FAKE, FAKE, a, FAKE, miss, miss, miss,
+                               err, 0)
+    _expect(uns, gu, T=3)                       # 24 rows
+    _expect(inv, gu, logits=None)
+    _expect(inv, gu, err=None)
+    _expect(inv, gu, a=FAKE + 4)                # a must be 16-byte aligned
+    _expect(inv, gu, w=wc)                      # S < E without a slot map
+    _expect(inv, gu, w=wc, slot_map=FAKE, miss=None)
+    _expect(uns, moe.moe_decode_down_combine, w, 3, cfg, FAKE, FAKE, FAKE, FAKE, bf, 0)
+    _expect(inv, moe.moe_decode_down_combine, w, 1, cfg, None, FAKE, FAKE, FAKE, bf, 0)
+    _expect(inv, moe.moe_decode_down_combine, w, 1, cfg, FAKE, FAKE, FAKE, FAKE, 9, 0)
+    # moe_route computes logits alone only with router weights and logits_out
+    _expect(inv, moe.moe_route, FAKE, bf, 1, 4096, FAKE, None, None, cfg, None, None, None, FAKE, 1 << 20, 0)
+    _expect(inv, moe.moe_route, None, bf, 1, 4096, None, FAKE, None, cfg, None, None, FAKE, None, 0, 0)

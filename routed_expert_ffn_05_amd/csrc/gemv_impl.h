@@ -1017,9 +1017,20 @@ __global__ __launch_bounds__(kDecThreads2) void decode_down_combine_kernel(const
     const int t = i / RB, hl = i - t * RB, h = h0 + hl;
     if (h >= H) continue;
     float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = t * k + j;
-      if (s_key[r] >= 0) acc = fmaf(s_w[r], yl[r * RB + hl], acc);
+    for (int j0 = 0; j0 < k; j0 += 8) {  // eight choices' operands read before their sums
+      int kk[8];
+      float ww[8], yy[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = t * k + j0 + u;
+        const bool in = j0 + u < k;
+        kk[u] = in ? s_key[r] : -1;
+        ww[u] = in ? s_w[r] : 0.0f;
+        yy[u] = in ? yl[r * RB + hl] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (kk[u] >= 0) acc = fmaf(ww[u], yy[u], acc);
     }
     if constexpr (ODT == DT_F32)
       static_cast<float*>(d.out)[size_t(t) * H + h] = acc;
@@ -1130,13 +1141,17 @@ hipError_t launch_decode_gate_up_t(const DecodeArgs& d, hipStream_t st) {
   constexpr int PB = dec_gu_pairs<LPR>();
   dim3 grid((d.I + PB - 1) / PB, kDecGroups), block(kThreads);
   const size_t lds = size_t(d.T) * d.H * (XT == DT_F32 ? 4 : 2) + size_t(d.E) * 4;
-  const void* kern = d.E <= 512 ? (const void*)decode_gate_up_kernel<WD, XT, LPR, CPL, 8>
-                                : (const void*)decode_gate_up_kernel<WD, XT, LPR, CPL, 16>;
+  // logits per lane of the top-k: the fewest that hold E (the selection does not depend on it)
+  const void* kern = d.E <= 384 ? (const void*)decode_gate_up_kernel<WD, XT, LPR, CPL, 6>
+                     : d.E <= 512 ? (const void*)decode_gate_up_kernel<WD, XT, LPR, CPL, 8>
+                                  : (const void*)decode_gate_up_kernel<WD, XT, LPR, CPL, 16>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  if (d.E <= 512)
+  if (d.E <= 384)
+    decode_gate_up_kernel<WD, XT, LPR, CPL, 6><<<grid, block, lds, st>>>(d);
+  else if (d.E <= 512)
     decode_gate_up_kernel<WD, XT, LPR, CPL, 8><<<grid, block, lds, st>>>(d);
   else
     decode_gate_up_kernel<WD, XT, LPR, CPL, 16><<<grid, block, lds, st>>>(d);

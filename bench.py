@@ -494,7 +494,7 @@ def run(args):
         fws_b = D.workspace(fb_bytes)
     # small decode batches: moe_layer's two-launch flow (routing + gate/up, down + combine), after
     # the router logits when router weights are given -- the same calls moe_layer makes
-    fused = not (tiers or lru) and moe.moe_layer_decode_fused(T, rcfg, desc, path, mode, xdt)
+    fused = not (tiers or lru or args.staged) and moe.moe_layer_decode_fused(T, rcfg, desc, path, mode, xdt)
     if fused:
         row_slot = torch.empty(R, dtype=torch.int32, device=dev)
         a_dec = torch.empty((R, I), dtype=torch.float32, device=dev)
@@ -873,6 +873,8 @@ def main(argv=None):
                     help="compact configs: resident slots from the hot-set planner instead of the seeded map")
     ap.add_argument("--graph-layers", type=int, default=0,
                     help="time the layer as replays of a HIP graph of this many layers (launch-bound batches)")
+    ap.add_argument("--staged", action="store_true",
+                    help="time the staged launches even where moe_layer takes the two-launch decode layer")
     ap.add_argument("--tiers", action="store_true",
                     help="compact configs: also compute the miss rows from a pool of the absent experts")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")

@@ -48,7 +48,7 @@ hipError_t launch_gemv_down(const GemvArgs& g, hipStream_t st);
 // gate/up in the first; down projection and combine in the second.
 constexpr int kDecMaxT = 4;    // tokens: one wave of a work-group selects each token's experts
 constexpr int kDecMaxR = 64;   // rows T*k: one wave holds the slot of every row
-constexpr int kDecFuseRows = 16;  // rows T*k up to which moe_layer takes the decode layer
+constexpr int kDecFuseRows = 16;  // rows T*k up to which moe_layer takes the decode layer (MXFP4; half for others)
 constexpr int kDecRB = 16;     // output columns per work-group of the down + combine launch
 struct DecodeArgs {
   int wdt, xdt, odt;
@@ -74,7 +74,7 @@ struct DecodeArgs {
   void* out;               // [T, H]
 };
 // whether the two-launch decode layer takes this shape (LDS budgets, row and token limits)
-bool decode_fused_fits(int T, int k, int E, int H, int I, int xdt);
+bool decode_fused_fits(int T, int k, int E, int H, int I, int xdt, int wdt);
 hipError_t launch_decode_gate_up(const DecodeArgs& d, hipStream_t st);
 hipError_t launch_decode_down_combine(const DecodeArgs& d, hipStream_t st);
 

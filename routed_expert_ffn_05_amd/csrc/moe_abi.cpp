@@ -615,7 +615,7 @@ int check_decode_shape(int T, const moe_routing* cfg, const moe_weights* w, int 
   MOE_TRY(check_T(T, cfg->k));
   MOE_TRY(check_weights(w));
   MOE_TRY(check_act_dtype(x_dtype, "x"));
-  if (!moe::decode_fused_fits(T, cfg->k, cfg->E, w->H, w->I, x_dtype))
+  if (!moe::decode_fused_fits(T, cfg->k, cfg->E, w->H, w->I, x_dtype, w->wdtype))
     return fail(MOE_ERR_UNSUPPORTED, "T = %d, k = %d, H = %d, I = %d: outside the two-launch decode layer", T, cfg->k,
                 w->H, w->I);
   return MOE_OK;
@@ -695,7 +695,7 @@ int moe_layer_decode_fused(int T, const moe_routing* cfg, const moe_weights* w, 
       check_path_mode(path, mode, w) != MOE_OK || check_act_dtype(x_dtype, "x") != MOE_OK)
     return -1;
   return resolve_path(path, T, cfg->k, w, mode) == MOE_PATH_GEMV && mode == MOE_MODE_A &&
-         moe::decode_fused_fits(T, cfg->k, cfg->E, w->H, w->I, x_dtype);
+         moe::decode_fused_fits(T, cfg->k, cfg->E, w->H, w->I, x_dtype, w->wdtype);
 }
 
 size_t moe_layer_workspace_size(int T, const moe_routing* cfg, const moe_weights* w, int path,

@@ -289,16 +289,18 @@ def test_layer_decode_fused_rule(L):
         c = moe.routing(E, k, "sigmoid")
         w = moe.weights(wd, E, 4096, I, FAKE, FAKE, FAKE, FAKE)
         return moe.moe_layer_decode_fused(T, c, w, path, mode, xdt)
-    assert fused(1) and fused(2) and fused(4, k=4)     # up to 16 rows
-    assert not fused(4)                                # 32 rows: the staged launches
-    assert not fused(5, k=2)                           # a fifth token
-    assert not fused(1, k=64, I=512)                   # 64 rows
-    assert fused(1, k=16, I=512)
-    assert not fused(2, I=8192)                        # the rows of a beyond the LDS budget
+    mx = moe.MOE_MXFP4
+    assert fused(1) and fused(2, k=4) and not fused(2)  # bf16: up to 8 rows
+    assert fused(2, wd=mx) and fused(4, k=4, wd=mx)     # MXFP4: up to 16 rows
+    assert not fused(4, wd=mx)                          # 32 rows: the staged launches
+    assert not fused(5, k=2)                            # a fifth token
+    assert not fused(1, k=64, I=512, wd=mx)             # 64 rows
+    assert fused(1, k=16, I=512, wd=mx)
+    assert not fused(2, I=8192, wd=mx)                  # the rows of a beyond the LDS budget
     assert not fused(0)
     assert not fused(1, wd=moe.MOE_FP8_E4M3_B128, mode=moe.MOE_MODE_B)      # mode B stays staged
-    assert not fused(2, wd=moe.MOE_FP8_E4M3_B128, path=moe.MOE_PATH_GEMM)   # the matrix-core path
-    assert fused(2, wd=moe.MOE_FP8_E4M3_B128, path=moe.MOE_PATH_AUTO)        # AUTO picks the GEMV here
+    assert not fused(1, wd=moe.MOE_FP8_E4M3_B128, path=moe.MOE_PATH_GEMM)   # the matrix-core path
+    assert fused(1, wd=moe.MOE_FP8_E4M3_B128, path=moe.MOE_PATH_AUTO)        # AUTO picks the GEMV here
     assert fused(1, xdt=moe.MOE_F32)
     _expect(moe.MOE_ERR_INVALID_ARG, fused, 1, xdt=7)
 

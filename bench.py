@@ -119,14 +119,14 @@ def _pmc_per_kernel(d, counter):
 
 def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kind, copy_bytes,
                   bytes_per_launch):
-    """PMC summary of the gate/up kernel `kind` (gemv | gemm | gemm_q).  The GEMM template serves
+    """PMC summary of the gate/up kernel `kind` (gemv | decode | gemm | gemm_q).  The GEMM template serves
     both projections; its gate/up instances are the ones whose second template argument is true."""
     kernel_key = GATE_UP_KERNELS[kind]
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
 
     def pick(dct, key):
-        ks = [k for k in dct if key in k and (kind == "gemv" or k.rstrip().endswith("true>"))]
+        ks = [k for k in dct if key in k and (kind in ("gemv", "decode") or k.rstrip().endswith("true>"))]
         if not ks:
             raise SystemExit(f"no kernel matching {key!r} in {sorted(dct)}")
         return dct[ks[0]]
@@ -142,7 +142,8 @@ def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, kind,
     kw = pick(write, kernel_key)
     fetch_b = sum(kf) / len(kf) * 1024.0 * (f_factor or 1.0)
     write_b = sum(kw) / len(kw) * 1024.0 * (w_factor or 1.0)
-    lines = [f"# HBM traffic of the gate/up {'GEMV' if kind == 'gemv' else 'grouped GEMM'} (rocprofv3 PMC)", "",
+    what = {"gemv": "GEMV", "decode": "launch of the two-launch decode layer (routing + gate/up)"}.get(kind, "grouped GEMM")
+    lines = [f"# HBM traffic of the gate/up {what} (rocprofv3 PMC)", "",
              f"fetch command: `{command_fetch}`", f"write command: `{command_write}`", "",
              f"kernel: `{kernel_key}`, dispatches: {len(kf)} (FETCH_SIZE), {len(kw)} (WRITE_SIZE)",
              f"copy probe: {copy_bytes} bytes; FETCH_SIZE {copy_f} KiB -> factor {f_factor}; "

@@ -10,6 +10,7 @@ and the two-tier identity of the MoET hybrid table rest on that); and the layer 
 tolerances.  Cases cover every weight format, both activation and output formats, router weights
 and given logits, softmax and sigmoid scores, a selection bias, compact maps, slots holding several
 rows of the batch, k = 16, E above 512, and the decode shapes at their stated sizes (T = 1)."""
+import dataclasses
 import sys
 
 import numpy as np
@@ -91,3 +92,30 @@ def test_fused_decode_equals_staged_launches(name):
         assert np.array_equal(lay["miss_expert"], ref["miss_expert"])
     print(f"[gpu-decode-fused] case={name}: identical to the staged launches", flush=True)
 
+
+
+def test_out_of_range_slot_map_entry_sets_device_error():
+    """A routed expert whose slot_map entry lies outside [-1, S) sets the device error word, as the
+    staged permutation does; a valid call writes the word back to zero."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import routed_expert_ffn_05_amd as moe
+    from gpu_cases import GpuCase
+    cfg = gen.config("compact_mxfp4", T=1, H=256, E=32, I=128, k=4, resident=10)
+    inp = gen.make_inputs(cfg)
+    lg = np.zeros((1, cfg.E), np.float32)
+    lg[0, [5, 6, 7, 8]] = [4.0, 3.0, 2.0, 1.0]       # the four chosen experts
+    inp.logits = lg
+    good = GpuCase(inp)
+    assert moe.moe_layer_decode_fused(cfg.T, good.route_cfg, good.w.desc, moe.MOE_PATH_GEMV, moe.MOE_MODE_A, good.xdt)
+    print("[gpu-decode-fused] error word: valid map", flush=True)
+    good.layer(path=moe.MOE_PATH_GEMV)              # no error raised: the word was written zero
+    for bad_entry in (cfg.S + 3, -7):
+        sm = inp.slot_map.copy()
+        sm[6] = bad_entry
+        inp_bad = dataclasses.replace(inp, slot_map=sm)
+        print(f"[gpu-decode-fused] error word: slot_map[6] = {bad_entry}", flush=True)
+        with pytest.raises(moe.MoeError) as ei:
+            GpuCase(inp_bad, dev_weights=good.w).layer(path=moe.MOE_PATH_GEMV)
+        assert ei.value.status == moe.MOE_ERR_DEVICE

@@ -3,10 +3,11 @@
 //   gate/up:  a[p, i] = silu(x_p . W_g[s,i,:]) * (x_p . W_u[s,i,:])  for the rows p of slot s
 //   down:     y[p, h] = a_p . W_d[s,h,:]
 //
-// Tiles.  A work-group (8 waves) computes a BM x BN output tile of one slot: each wave owns 32 of
-// the BN = 256 columns and up to 4 MFMA row blocks of 32 rows; a tile whose slot has fewer rows
-// runs only ceil(rows/32) row blocks, so a slot of n rows costs that much matrix work while its
-// weights are streamed once per 128-row M tile.  The wide N tile halves how often each activation
+// Tiles.  A work-group (8 waves) computes a BM x BN output tile of one slot.  A tile whose slot
+// has fewer than 128 rows runs only ceil(rows/32) MFMA row blocks of 32 rows (each wave: 32 of the
+// BN = 256 columns, all row blocks), so a slot of n rows costs that much matrix work while its
+// weights are streamed once per 128-row M tile; a full tile of bf16 or FP8 weights runs on a 2 x 4
+// grid of waves of 64 x 64 (2 x 2 MFMA blocks, so each LDS fragment feeds two instructions).  The wide N tile halves how often each activation
 // row is moved from L2 into LDS (the on-chip traffic that bounds these GEMMs).
 // Staging.  Operand tiles of each K step (BK = 128 for FP8 and MXFP4 weights, 64 for bf16: a
 // weight row segment per step is a whole 128-byte line where LDS allows) move from HBM to LDS by
@@ -85,26 +86,42 @@ __host__ __device__ constexpr size_t row_bytes(int K) {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Down epilogue: the tile's y (rows x 256 columns, fp32; accumulator r of lane l is row
-// 8*(r/4) + 4*(l/32) + r%4 of its row block, column 32*wave + l%32) leaves through LDS in
-// 16-byte pieces, 64 rows at a time (row stride 264 floats: the two lane halves, 4 rows apart,
-// write disjoint bank halves).  y is read once, by the combine, long after: the stores are
+// 8*(r/4) + 4*(l/32) + r%4 of its row block, column l%32 of its column block) leaves through LDS
+// in 16-byte pieces, 64 rows at a time (row stride 264 floats: the two lane halves, 4 rows apart,
+// write disjoint bank halves).  acc[i][c] is row block i, column block c of the wave: with the
+// 2 x 4 wave grid (TD) wave w holds rows 64(w/4) + 32i.., columns 64(w%4) + 32c..; otherwise
+// rows 32i.., columns 32w...  y is read once, by the combine, long after: the stores are
 // non-temporal.  Needs N % 4 == 0 and 64 * 264 * 4 bytes of `lds`; every wave's stage reads and
-// direct loads must be done (the caller waited for its loads).
-template <int NS, typename Acc>
-__device__ __forceinline__ void store_y_tile(const Acc& acc, uint8_t* lds, float* __restrict__ y, int m0, int rows,
-                                             int n0, int N) {
+// direct loads must be done (the caller waited for its loads).  acc(i, c, r) reads register r of
+// accumulator block (i, c).
+template <int NR, int NC, bool TD, typename Acc>
+__device__ __forceinline__ void store_y_tile(Acc acc, uint8_t* lds, float* __restrict__ y, int m0, int rows,
+                                             int n0, int N, int halves) {
   constexpr int YS = 264;
   float* yt = reinterpret_cast<float*>(lds);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ln = lane & 31, kh = lane >> 5;
-#pragma unroll
-  for (int half = 0; half < (NS + 1) / 2; ++half) {
+  for (int half = 0; half < halves; ++half) {
     __syncthreads();  // the stages (first half) or the previous half's rows are no longer read
+    if constexpr (TD) {
+      if ((wv >> 2) == half) {
 #pragma unroll
-    for (int mh = 0; mh < 2; ++mh) {
-      const int ms = 2 * half + mh;
-      if (ms < NS) {
+        for (int i = 0; i < NR; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) yt[(mh * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * YS + 32 * wv + ln] = acc[ms][r];
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              yt[(i * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * YS + 64 * (wv & 3) + 32 * c + ln] = acc(i, c, r);
+      }
+    } else {
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          if (i == 2 * half + mh) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yt[(mh * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * YS + 32 * wv + ln] = acc(i, 0, r);
+          }
+        }
       }
     }
     __syncthreads();
@@ -213,16 +230,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     }
     rowok[tid] = ok;
   }
-  // B column of this lane (a row of the weight tile)
-  const int bl = GATEUP ? (ln < 16 ? 16 * wv + ln : BN / 2 + 16 * wv + (ln - 16)) : 32 * wv + ln;
   constexpr bool kBlockScaled = WD == DT_FP8;
-  int srow = 0;
+  // the tile's B rows lie in at most four 128-row scale blocks: those of tile rows 0, 127, 128
+  // and 255 (gate/up: the gate rows start on a block boundary, the up rows may straddle one);
+  // srow_of(c) is the one of tile row c
+  int blk[4] = {0, 0, 0, 0};
+  auto srow_of = [&](int c) -> int {
+    const int gb = brow_clamped(c) >> 7;
+    return gb == blk[0] ? 0 : gb == blk[1] ? 1 : gb == blk[2] ? 2 : 3;
+  };
   if constexpr (kBlockScaled) {
-    // the tile's B rows lie in at most four 128-row scale blocks: those of tile rows 0, 127, 128
-    // and 255 (gate/up: the gate rows start on a block boundary, the up rows may straddle one)
     const int KB = (K + 127) >> 7;
     const int NBk = (N + 127) >> 7;
-    int blk[4];
     blk[0] = brow_clamped(0) >> 7;
     blk[1] = brow_clamped(127) >> 7;
     blk[2] = brow_clamped(128) >> 7;
@@ -232,8 +251,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       const int r = t / KB, kb = t - r * KB;
       Ssc[r][kb] = sbase[size_t(blk[r]) * KB + kb];
     }
-    const int gb = brow_clamped(bl) >> 7;
-    srow = gb == blk[0] ? 0 : gb == blk[1] ? 1 : gb == blk[2] ? 2 : 3;
   }
   // MXFP4: E8M0 scales of the tile's rows over all of K, [row][K/32] in LDS (K/32 is even).
   // With K % 512 == 0 a row is gpr whole 16-byte granules, stored rotated by a per-row key so that
@@ -256,7 +273,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       }
     }
   }
-  const int fp4_row = bl * KB32, fp4_keyl = fp4_key(bl);
 
   // K steps: the weights' K once, or (down with a split a) twice, first against the hi halves of
   // a, then against the lo halves; kwof(kk) is the weights' K step of step kk
@@ -264,8 +280,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   const int nk = GATEUP ? nkw : nkw * asplit;
   auto kwof = [&](int kk) -> int { return kk >= nkw ? kk - nkw : kk; };
 
+  // Wave layouts.  A tile of NS < 4 row blocks (and every MXFP4 tile): wave w owns MFMA column
+  // block w (32 B columns) and all NS row blocks, so each B fragment feeds NS matrix instructions.
+  // A full tile of bf16 or FP8 weights (4 row blocks): the waves form a 2 x 4 grid, wave w owning row blocks 2(w/4), 2(w/4)+1 and column
+  // blocks 2(w%4), 2(w%4)+1, so each A and each B fragment feeds two matrix instructions (the
+  // LDS bytes read per instruction fall by a third for FP8 weights; the two waves on a SIMD,
+  // w and w+4, share its matrix core evenly).  Column block q holds B rows 16q..16q+15 of the
+  // gate half and the same rows of the up half (gate/up), or rows 32q..32q+31 (down), so that
+  // lanes l and l+16 of a gate/up block hold gate and up of the same output column.
+  auto bcol = [&](int q) -> int {
+    return GATEUP ? (ln < 16 ? 16 * q + ln : BN / 2 + 16 * q + (ln - 16)) : 32 * q + ln;
+  };
   auto run = [&](auto ns_c) {
     constexpr int NS = decltype(ns_c)::value;
+    // 2 x 4 wave grid for full tiles of bf16 and FP8 weights (MXFP4 tiles measured slower with it:
+    // each column block adds its own scale reads and conversions)
+    constexpr bool TD = NS == 4 && WD != DT_MXFP4;
+    constexpr int NR = TD ? 2 : NS, NC = TD ? 2 : 1;  // row and column blocks of a wave
+    const int rbase = TD ? 64 * (wv >> 2) : 0;        // first tile row of the wave's row blocks
+    int blc[NC], srowc[NC], fp4_row[NC], fp4_keyl[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      blc[c] = bcol(TD ? 2 * (wv & 3) + c : wv);
+      srowc[c] = kBlockScaled ? srow_of(blc[c]) : 0;
+      fp4_row[c] = blc[c] * KB32;
+      fp4_keyl[c] = fp4_key(blc[c]);
+    }
     constexpr int AB = NS * 32 * F::AROW;             // A bytes per stage
     constexpr int NA = AB / 1024;                     // A chunks per step
     constexpr int A_HI = (NA + kWaves - 1) / kWaves;  // A chunks of waves 0 .. NA%8-1 (or all)
@@ -273,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     constexpr int NST = F::nstage(NS);                // K steps in flight
     constexpr int SB = F::stage_bytes(NS);            // bytes per stage: A rows, then the B tile
     constexpr int KS = F::KS;                         // MFMA K sub-steps per step
-    constexpr int kReads = NS + (WD == DT_MXFP4 ? 2 : 1);  // LDS reads per sub-step
+    constexpr int kReads = NR + NC * (WD == DT_MXFP4 ? 2 : 1);  // LDS reads per sub-step
     static_assert(NST >= 2, "LDS budget");
     const int na = (NA % kWaves == 0 || wv < NA % kWaves) ? A_HI : A_LO;  // this wave's A chunks
     const int nl = na + F::INSTR;                                       // its loads per step
@@ -307,59 +347,66 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         if (j < nl && j >= (nl * g) / KG && j < (nl * (g + 1)) / KG) issue_one(j, kk, st);
     };
 
-    f32x16_t acc[NS], tmp[NS];
+    f32x16_t acc[NR][NC], tmp[NR][NC];
 #pragma unroll
-    for (int ms = 0; ms < NS; ++ms)
+    for (int i = 0; i < NR; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[ms][r] = tmp[ms][r] = 0.0f;
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][c][r] = tmp[i][c][r] = 0.0f;
 
     // raw LDS fragments of one K sub-step: A rows as bf16, B in its stored format (+ MXFP4 scale)
     struct Raw {
-      bf16x8_t a[NS];
-      uint32_t b[WD == DT_BF16 ? 4 : WD == DT_FP8 ? 2 : 1];
-      uint32_t sc;
+      bf16x8_t a[NR];
+      uint32_t b[NC][WD == DT_BF16 ? 4 : WD == DT_FP8 ? 2 : 1];
+      uint32_t sc[NC];
     };
     auto load_raw = [&](const uint8_t* st, int kk, int ks, Raw& f) {
 #pragma unroll
-      for (int ms = 0; ms < NS; ++ms) {
-        const int m = ms * 32 + ln;
-        f.a[ms] = *reinterpret_cast<const bf16x8_t*>(st + m * F::AROW + swzA(m, ks * 2 + kh) * 16);
+      for (int i = 0; i < NR; ++i) {
+        const int m = rbase + i * 32 + ln;
+        f.a[i] = *reinterpret_cast<const bf16x8_t*>(st + m * F::AROW + swzA(m, ks * 2 + kh) * 16);
       }
       const uint8_t* B = st + AB;
-      if constexpr (WD == DT_BF16) {
-        const uint4 q = *reinterpret_cast<const uint4*>(B + bl * 128 + swz128(bl, ks * 2 + kh) * 16);
-        f.b[0] = q.x; f.b[1] = q.y; f.b[2] = q.z; f.b[3] = q.w;
-      } else if constexpr (WD == DT_FP8) {  // 128 K per row: granule ks holds K [16ks, 16ks+16)
-        const uint2 q = *reinterpret_cast<const uint2*>(B + bl * 128 + swz128(bl, ks) * 16 + kh * 8);
-        f.b[0] = q.x; f.b[1] = q.y;
-      } else {  // 64-byte rows of 128 K: granule ks/2 holds K [32(ks/2), +32)
-        f.b[0] = *reinterpret_cast<const uint32_t*>(B + bl * 64 + swz64(bl, ks >> 1) * 16 + (ks & 1) * 8 + kh * 4);
-        const int kb = kwof(kk) * (BK / 32) + (ks >> 1);
-        if (fp4_async) {
-          int slot = (kb >> 4) + fp4_keyl;
-          slot -= slot >= gpr ? gpr : 0;
-          f.sc = Sfp4[fp4_row + slot * 16 + (kb & 15)];
-        } else {
-          f.sc = Sfp4[fp4_row + kb];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int bl = blc[c];
+        if constexpr (WD == DT_BF16) {
+          const uint4 q = *reinterpret_cast<const uint4*>(B + bl * 128 + swz128(bl, ks * 2 + kh) * 16);
+          f.b[c][0] = q.x; f.b[c][1] = q.y; f.b[c][2] = q.z; f.b[c][3] = q.w;
+        } else if constexpr (WD == DT_FP8) {  // 128 K per row: granule ks holds K [16ks, 16ks+16)
+          const uint2 q = *reinterpret_cast<const uint2*>(B + bl * 128 + swz128(bl, ks) * 16 + kh * 8);
+          f.b[c][0] = q.x; f.b[c][1] = q.y;
+        } else {  // 64-byte rows of 128 K: granule ks/2 holds K [32(ks/2), +32)
+          f.b[c][0] = *reinterpret_cast<const uint32_t*>(B + bl * 64 + swz64(bl, ks >> 1) * 16 + (ks & 1) * 8 + kh * 4);
+          const int kb = kwof(kk) * (BK / 32) + (ks >> 1);
+          if (fp4_async) {
+            int slot = (kb >> 4) + fp4_keyl[c];
+            slot -= slot >= gpr ? gpr : 0;
+            f.sc[c] = Sfp4[fp4_row[c] + slot * 16 + (kb & 15)];
+          } else {
+            f.sc[c] = Sfp4[fp4_row[c] + kb];
+          }
         }
       }
     };
-    // B fragment as bf16 (e4m3fn -> bf16 exact; e2m1 x power-of-two scale -> bf16 exact)
-    auto decode_b = [&](const Raw& f) -> bf16x8_t {
+    // B fragment of column block c as bf16 (e4m3fn -> bf16 exact; e2m1 x power-of-two scale ->
+    // bf16 exact)
+    auto decode_b = [&](const Raw& f, int c) -> bf16x8_t {
       uint32_t o[4];
       if constexpr (WD == DT_BF16) {
-        o[0] = f.b[0]; o[1] = f.b[1]; o[2] = f.b[2]; o[3] = f.b[3];
+        o[0] = f.b[c][0]; o[1] = f.b[c][1]; o[2] = f.b[c][2]; o[3] = f.b[c][3];
       } else if constexpr (WD == DT_FP8) {
-        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[0], 1.0f, false));
-        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[0], 1.0f, true));
-        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[1], 1.0f, false));
-        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[1], 1.0f, true));
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[c][0], 1.0f, false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[c][0], 1.0f, true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[c][1], 1.0f, false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.b[c][1], 1.0f, true));
       } else {
-        const float sc = e8m0_to_f32(f.sc);
-        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[0], sc, 0));
-        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[0], sc, 1));
-        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[0], sc, 2));
-        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[0], sc, 3));
+        const float sc = e8m0_to_f32(f.sc[c]);
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[c][0], sc, 0));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[c][0], sc, 1));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[c][0], sc, 2));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.b[c][0], sc, 3));
       }
       return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
     };
@@ -405,57 +452,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) load_raw(st, kk, ks + 1, f[(ks + 1) & 1]);
         issue_group(ks, kn, wst);
-        const bf16x8_t b = decode_b(f[ks & 1]);
 #pragma unroll
-        for (int ms = 0; ms < NS; ++ms) {
-          if constexpr (kBlockScaled)
-            tmp[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].a[ms], b, tmp[ms], 0, 0, 0);
-          else
-            acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].a[ms], b, acc[ms], 0, 0, 0);
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8_t b = decode_b(f[ks & 1], c);
+#pragma unroll
+          for (int i = 0; i < NR; ++i) {
+            if constexpr (kBlockScaled)
+              tmp[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].a[i], b, tmp[i][c], 0, 0, 0);
+            else
+              acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].a[i], b, acc[i][c], 0, 0, 0);
+          }
         }
         // keep the next sub-step's LDS reads ahead of this sub-step's matrix instructions
         if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NR * NC, 0);
       }
       if constexpr (kBlockScaled) {
-        // a step is one 128-wide K block: fold its partial sums in with the block's scale
-        const float sc = Ssc[srow][kwof(kk)];
+        // a step is one 128-wide K block: fold its partial sums in with the blocks' scales
 #pragma unroll
-        for (int ms = 0; ms < NS; ++ms)
+        for (int c = 0; c < NC; ++c) {
+          const float sc = Ssc[srowc[c]][kwof(kk)];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc[ms][r] = fmaf(sc, tmp[ms][r], acc[ms][r]);
-            tmp[ms][r] = 0.0f;
-          }
+          for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              acc[i][c][r] = fmaf(sc, tmp[i][c][r], acc[i][c][r]);
+              tmp[i][c][r] = 0.0f;
+            }
+        }
       }
     }
     wait_vmcnt<0>();  // the trailing re-loads must land before the work-group's LDS is released
 
     // ---- epilogue: accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4 of its row block,
-    // column l%32
+    // column l%32 of its column block
     if constexpr (GATEUP) {
       // a = silu(g) * u in bf16 goes through LDS so that it leaves in whole 16-byte pieces per
       // lane (the accumulator layout gives 2-byte pieces, 16 lanes to a row segment)
       uint16_t* at = reinterpret_cast<uint16_t*>(smem);  // [BM][128] bf16
       __syncthreads();  // every wave's direct loads have landed and its stage reads are done
 #pragma unroll
-      for (int ms = 0; ms < NS; ++ms) {
+      for (int i = 0; i < NR; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          // registers r, r+1 are rows m, m+1; lane ln < 16 holds gate values, lane ln + 16 the up
-          // values of the same columns.  One exchange gives the low lane (gate, up) of row m and
-          // the high lane those of row m+1, so each lane forms one silu(g)*u per register pair.
-          const bool lo = ln < 16;
-          const float x0 = acc[ms][r], x1 = acc[ms][r + 1];
-          const float recv = __shfl_xor(lo ? x1 : x0, 16);
-          const float g = lo ? x0 : recv, u = lo ? recv : x1;
-          const int m = ms * 32 + 8 * (r >> 2) + 4 * kh + (r & 3) + (lo ? 0 : 1);
-          if (m < rows) {
-            const float a = rowok[m] ? silu_fast(g) * u : 0.0f;
-            const uint16_t hi = f32_to_bf16(a);
-            at[m * 128 + 16 * wv + (ln & 15)] = hi;
-            // split a: the rounding error of the hi half, itself rounded to bf16 (a to ~16 bits)
-            if (asplit == 2) at[BM * 128 + m * 128 + 16 * wv + (ln & 15)] = f32_to_bf16(a - bf16_to_f32(hi));
+        for (int c = 0; c < NC; ++c) {
+          const int col = 16 * (TD ? 2 * (wv & 3) + c : wv) + (ln & 15);  // output column in the tile
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            // registers r, r+1 are rows m, m+1; lane ln < 16 holds gate values, lane ln + 16 the
+            // up values of the same columns.  One exchange gives the low lane (gate, up) of row m
+            // and the high lane those of row m+1, so each lane forms one silu(g)*u per pair.
+            const bool lo = ln < 16;
+            const float x0 = acc[i][c][r], x1 = acc[i][c][r + 1];
+            const float recv = __shfl_xor(lo ? x1 : x0, 16);
+            const float g = lo ? x0 : recv, u = lo ? recv : x1;
+            const int m = rbase + i * 32 + 8 * (r >> 2) + 4 * kh + (r & 3) + (lo ? 0 : 1);
+            if (m < rows) {
+              const float a = rowok[m] ? silu_fast(g) * u : 0.0f;
+              const uint16_t hi = f32_to_bf16(a);
+              at[m * 128 + col] = hi;
+              // split a: the rounding error of the hi half, itself rounded to bf16 (a to ~16 bits)
+              if (asplit == 2) at[BM * 128 + m * 128 + col] = f32_to_bf16(a - bf16_to_f32(hi));
+            }
           }
         }
       }
@@ -470,7 +527,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
               *reinterpret_cast<const uint4*>(at + half * BM * 128 + m * 128 + c8);
       }
     } else {
-      store_y_tile<NS>(acc, smem, static_cast<float*>(out), m0, rows, n0, N);
+      store_y_tile<NR, NC, TD>([&](int i, int c, int r) { return acc[i][c][r]; }, smem, static_cast<float*>(out), m0,
+                               rows, n0, N, (NS + 1) / 2);
     }
   };
   switch (nsub) {
@@ -802,7 +860,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(
         if (part == 0) as_out[size_t(m0 + m) * KB + (n0 >> 5) + blk] = uint8_t(X + 127);
       }
     } else {
-      store_y_tile<NS>(acc, smem, out, m0, rows, n0, N);
+      store_y_tile<NS, 1, false>([&](int i, int, int r) { return acc[i][r]; }, smem, out, m0, rows, n0, N, (NS + 1) / 2);
     }
   };
   switch (nsub) {

@@ -631,9 +631,10 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
 //   each row (-1 when the row has none) for the second launch, the compact miss list (rows in
 //   ascending r), the miss count and the error word.
 // decode_down_combine_kernel: a work-group owns RB consecutive output columns for every row: it
-//   loads all rows of a into LDS (direct LDS loads, in flight with the row slots), computes y for
-//   each resident slot's rows, NSL slots' weight loads in flight together, keeps y in LDS and
-//   sums out[t] = sum_j w[t,j] * y[t*k+j] over the computed rows in ascending j.
+//   loads all rows of a into LDS (direct LDS loads, in flight with the row slots, or with MXFP4
+//   weights with the first slots' weights), computes y for each resident slot's rows, NSL slots'
+//   weight loads in flight together, keeps y in LDS and sums out[t] = sum_j w[t,j] * y[t*k+j] over
+//   the computed rows in ascending j.
 //
 // Every element is formed as on the GEMV path (same lanes per row and chunks per lane, so the
 // same partial sums in the same order and the same segmented reduction; the same combine order),
@@ -890,26 +891,31 @@ __global__ __launch_bounds__(kDecThreads2) void decode_down_combine_kernel(const
   float* yl = reinterpret_cast<float*>(dl + size_t(R) * arow);      // [R][RB]
   const int h0 = blockIdx.x * RB;
 
-  // 1. every row of a (direct LDS loads, 1 KB per wave instruction) and the rows' slots and gates
-  const int ng = R * (I >> 2);
-  const uint32_t abase = lds_addr(al);
-  for (int c0 = wid * 64; c0 < ng; c0 += kDecThreads2)
-    if (c0 + lane < ng) dma16(reinterpret_cast<const uint8_t*>(d.a) + size_t(c0 + lane) * 16, abase + uint32_t(c0) * 16);
+  // every row of a (direct LDS loads, 1 KB per wave instruction)
+  auto load_a = [&]() {
+    const int ng = R * (I >> 2);
+    const uint32_t abase = lds_addr(al);
+    for (int c0 = wid * 64; c0 < ng; c0 += kDecThreads2)
+      if (c0 + lane < ng) dma16(reinterpret_cast<const uint8_t*>(d.a) + size_t(c0 + lane) * 16, abase + uint32_t(c0) * 16);
+  };
+  // MXFP4 weights (small slot slices): the first slots' weight loads are issued before the rows of
+  // a, which they do not depend on, so both fly together; bf16 and FP8 slices measured faster with
+  // a first
+  constexpr bool kEarlyW = WD == DT_MXFP4;
+  if constexpr (!kEarlyW) load_a();
+
+  // 1. the rows' slots and gates
   int key = -1;
   float gw = 0.0f;
   if (lane < R) {
     key = d.rkey[lane];
     gw = d.topk_w[lane];
   }
-  wait_vmcnt<0>();
   if (key < 0 || key >= S) key = -1;
   if (wid == 0 && lane < R) {
     s_key[lane] = key;
     s_w[lane] = gw;
   }
-  __syncthreads();
-
-  // 2. y of every resident slot's rows for this work-group's columns
   bool lead = key >= 0;  // the first row of its slot
   for (int q = 0; q < R; ++q) {
     const int kq = __builtin_amdgcn_readlane(key, q);
@@ -920,9 +926,14 @@ __global__ __launch_bounds__(kDecThreads2) void decode_down_combine_kernel(const
   const int CPR = I / EPC;
   const size_t rb = row_bytes<WD>(I);
   const int hb = h0 + ((wid % kWaves) * GPW + grp) * ROWS;  // this lane group's first output row
-  while (rest) {
-    int sv[NSL];
-    unsigned long long rm[NSL];
+
+  // 2. y of every resident slot's rows for this work-group's columns, NSL slots' weights in flight
+  // at a time
+  int sv[NSL];
+  unsigned long long rm[NSL];
+  uint4 q[NSL][ROWS][CPL];
+  uint32_t sb[NSL][ROWS][CPL];
+  auto load_batch = [&]() {
 #pragma unroll
     for (int u = 0; u < NSL; ++u) {
       sv[u] = -1;
@@ -933,8 +944,6 @@ __global__ __launch_bounds__(kDecThreads2) void decode_down_combine_kernel(const
         rm[u] = __ballot(key == sv[u]);
       }
     }
-    uint4 q[NSL][ROWS][CPL];
-    uint32_t sb[NSL][ROWS][CPL];
 #pragma unroll
     for (int u = 0; u < NSL; ++u) {
       const int su = sv[u] < 0 ? 0 : sv[u];
@@ -956,6 +965,8 @@ __global__ __launch_bounds__(kDecThreads2) void decode_down_combine_kernel(const
         }
       }
     }
+  };
+  auto compute_batch = [&]() {
 #pragma unroll
     for (int u = 0; u < NSL; ++u) {
       unsigned long long mm = rm[u];
@@ -1009,6 +1020,17 @@ __global__ __launch_bounds__(kDecThreads2) void decode_down_combine_kernel(const
           }
       }
     }
+  };
+  if constexpr (kEarlyW) {
+    load_batch();
+    load_a();
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  if constexpr (kEarlyW) compute_batch();
+  while (rest) {
+    load_batch();
+    compute_batch();
   }
   __syncthreads();
 

@@ -270,7 +270,7 @@ int moe_layer(const void* x, int x_dtype, int T, const float* w_router, const fl
 
 /* ------------------------------------------------------------------------------------------
  * moe_layer_decode_fused -- whether moe_layer runs this batch as the two-launch decode layer.
- * It does for T <= 4 tokens and T*k <= 16 rows (MXFP4 weights; 8 rows for the others, whose
+ * It does for T <= 4 tokens and T*k <= 32 rows (MXFP4 weights; 8 rows for the others, whose
  * bytes per slot stream better on the staged launches once a batch touches many slots) on the
  * GEMV path (`path` resolved as
  * moe_resolve_path does) in mode A, when the two launches' LDS fits: T rows of x plus the E-entry
@@ -292,7 +292,7 @@ int moe_layer_decode_fused(int T, const moe_routing* cfg, const moe_weights* w, 
  * moe_decode_gate_up, moe_decode_down_combine -- the two launches of the decode layer, for
  * callers that schedule them themselves (moe_layer makes exactly these calls, after the router
  * logits when router weights are given).  Shapes as moe_layer_decode_fused requires (T <= 4,
- * T*k <= 16 or 8, the LDS rule); MOE_ERR_UNSUPPORTED otherwise.  Call them in order on one stream.
+ * T*k <= 32 or 8, the LDS rule); MOE_ERR_UNSUPPORTED otherwise.  Call them in order on one stream.
  *
  * moe_decode_gate_up: routing (top-k of the given logits, scores and gates as moe_route), the
  * slot of each row, the compact miss list (as moe_permute) and a = silu(x W_g^T) * (x W_u^T) of

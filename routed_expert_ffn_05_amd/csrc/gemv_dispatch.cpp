@@ -48,7 +48,7 @@ hipError_t launch_gemv_down(const GemvArgs& g, hipStream_t st) {
 // 36.0, T=2 55.3 vs 53.6.  Then the LDS: the T token rows and the slot map; every row of a and y.
 bool decode_fused_fits(int T, int k, int E, int H, int I, int xdt, int wdt) {
   const long long rows = (long long)T * k;
-  const int max_rows = wdt == DT_MXFP4 ? kDecFuseRows : kDecFuseRows / 2;
+  const int max_rows = wdt == DT_MXFP4 ? kDecFuseRows : kDecFuseRowsWide;
   if (T < 1 || T > kDecMaxT || k < 1 || rows > max_rows || E < 1 || E > 1024) return false;
   const size_t R = size_t(rows);
   const size_t lds_gu = size_t(T) * H * (xdt == DT_F32 ? 4 : 2) + size_t(E) * 4;

@@ -48,7 +48,8 @@ hipError_t launch_gemv_down(const GemvArgs& g, hipStream_t st);
 // gate/up in the first; down projection and combine in the second.
 constexpr int kDecMaxT = 4;    // tokens: one wave of a work-group selects each token's experts
 constexpr int kDecMaxR = 64;   // rows T*k: one wave holds the slot of every row
-constexpr int kDecFuseRows = 16;  // rows T*k up to which moe_layer takes the decode layer (MXFP4; half for others)
+constexpr int kDecFuseRows = 32;      // rows T*k up to which moe_layer takes the decode layer (MXFP4 weights)
+constexpr int kDecFuseRowsWide = 8;   // the same for bf16, FP8 and fp32 weights
 constexpr int kDecRB = 16;     // output columns per work-group of the down + combine launch
 struct DecodeArgs {
   int wdt, xdt, odt;

@@ -291,8 +291,8 @@ def test_layer_decode_fused_rule(L):
         return moe.moe_layer_decode_fused(T, c, w, path, mode, xdt)
     mx = moe.MOE_MXFP4
     assert fused(1) and fused(2, k=4) and not fused(2)  # bf16: up to 8 rows
-    assert fused(2, wd=mx) and fused(4, k=4, wd=mx)     # MXFP4: up to 16 rows
-    assert not fused(4, wd=mx)                          # 32 rows: the staged launches
+    assert fused(2, wd=mx) and fused(4, wd=mx)          # MXFP4: up to 32 rows
+    assert not fused(4, k=16, wd=mx)                    # 64 rows: the staged launches
     assert not fused(5, k=2)                            # a fifth token
     assert not fused(1, k=64, I=512, wd=mx)             # 64 rows
     assert fused(1, k=16, I=512, wd=mx)

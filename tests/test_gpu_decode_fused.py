@@ -1,4 +1,4 @@
-"""GPU: the two-launch decode layer.  For batches of at most 4 tokens and 16 rows (MXFP4; 8 rows for the other formats) on the GEMV path
+"""GPU: the two-launch decode layer.  For batches of at most 4 tokens and 32 rows (MXFP4; 8 rows for the other formats) on the GEMV path
 (mode A) moe_layer runs the layer in two launches: every work-group of the first selects the
 batch's experts itself and computes gate/up for one slot, the second computes the down projection
 of every row for a block of output columns and combines in place.  The staged launches (route and
@@ -32,6 +32,7 @@ CASES = {
     # MXFP4 compact maps (rows routed to absent experts go to the miss list)
     "mxfp4_compact_T1": (gen.config("compact_mxfp4", T=1, H=512, E=96, I=256, k=8, resident=30), False),
     "mxfp4_compact_T4": (gen.config("compact_mxfp4", T=4, H=512, E=96, I=256, k=4, resident=30), False),
+    "mxfp4_compact_T4_k8": (gen.config("compact_mxfp4", T=4, H=512, E=96, I=256, k=8, resident=40), False),
     "mxfp4_E600_k16": (gen.config("compact_mxfp4", T=1, H=256, E=600, I=128, k=16, resident=200), False),
     # fp32 weights and activations, softmax scores
     "f32_softmax": (gen.config("tiny", T=2, H=256, E=8, I=128, k=2), False),
@@ -40,6 +41,7 @@ CASES = {
     "k16_T1": (gen.config("compact_mxfp4", T=1, H=256, E=128, I=128, k=16, resident=100), False),
     # the decode shapes at their stated sizes
     "compact_mxfp4_T1_full": (gen.config("compact_mxfp4", T=1), False),
+    "compact_mxfp4_T4_full": (gen.config("compact_mxfp4", T=4), False),
     "decode_fp8_T1_full": (gen.config("decode_fp8", T=1), False),
     "decode_bf16_T1_full": (gen.config("decode_bf16", T=1), False),
 }

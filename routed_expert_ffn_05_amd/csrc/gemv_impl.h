@@ -40,7 +40,16 @@ namespace gemv {
 #define MOE_GEMV_LOADS_DOWN 4     // down (short rows of I elements): the same, per row step
 #endif
 #ifndef MOE_GEMV_TARGET_BLOCKS
-#define MOE_GEMV_TARGET_BLOCKS 4096  // fewer row steps per work-group until the grid has this many
+#define MOE_GEMV_TARGET_BLOCKS 4096  // fewer row steps per work-group until the grid has this many,
+#endif
+#ifndef MOE_GEMV_TARGET_BLOCKS_MAX
+#define MOE_GEMV_TARGET_BLOCKS_MAX 8192  // and on to this many while the byte floors below hold
+#endif
+#ifndef MOE_GEMV_WG_BYTES_GU
+#define MOE_GEMV_WG_BYTES_GU 65536   // gate/up: weight bytes a work-group streams, at least
+#endif
+#ifndef MOE_GEMV_WG_BYTES_DN
+#define MOE_GEMV_WG_BYTES_DN 32768   // down: the same
 #endif
 #ifndef MOE_GEMV_NT
 #define MOE_GEMV_NT 1             // non-temporal (streaming) weight loads
@@ -1079,12 +1088,18 @@ inline void pick_lpr_cpl(int CPR, int& lpr, int& cpl) {
   }
 }
 
-// row steps per wave: enough work-groups to fill the chip when few slots are active
-inline int pick_iters(int rows_total, int rows_per_block_step, int n_ord) {
+// row steps per wave: enough work-groups to fill the chip when few slots are active, and more (up
+// to the larger target) while each still streams floor_bytes of weights (timed together: decode
+// bf16 T=4 gate/up 80.0 -> 75.7 us with one row step, while FP8 rows, half as long, and the down
+// projection's short rows measured slower below the floors)
+inline int pick_iters(int rows_total, int rows_per_block_step, int n_ord, size_t bytes_per_block_step,
+                      size_t floor_bytes) {
   int iters = kIters;
   while (iters > 1) {
     const int blocks = (rows_total + rows_per_block_step * iters - 1) / (rows_per_block_step * iters);
-    if ((long long)blocks * n_ord >= MOE_GEMV_TARGET_BLOCKS) break;
+    const long long grid = (long long)blocks * n_ord;
+    if (grid >= MOE_GEMV_TARGET_BLOCKS_MAX) break;
+    if (grid >= MOE_GEMV_TARGET_BLOCKS && bytes_per_block_step * size_t(iters / 2) < floor_bytes) break;
     iters >>= 1;
   }
   return iters;
@@ -1095,7 +1110,7 @@ hipError_t launch_gate_up_t(const GemvArgs& g, hipStream_t st) {
   constexpr int ROWS = rows_per_step<CPL>();
   constexpr int PAIRS = ROWS / 2 > 0 ? ROWS / 2 : 1;
   const int step = kWaves * (64 / LPR) * PAIRS;
-  const int iters = pick_iters(g.I, step, g.n_ord);
+  const int iters = pick_iters(g.I, step, g.n_ord, size_t(step) * 2 * row_bytes<WD>(g.H), MOE_GEMV_WG_BYTES_GU);
   dim3 grid((g.I + step * iters - 1) / (step * iters), g.n_ord), block(kThreads);
   const size_t lds = size_t(kTokL) * g.H * (XT == DT_F32 ? 4 : 2);
   if (lds > 65536) {
@@ -1112,7 +1127,7 @@ template <int WD, int LPR, int CPL, int LOADS = MOE_GEMV_LOADS_DOWN>
 hipError_t launch_down_t(const GemvArgs& g, hipStream_t st) {
   constexpr int ROWS = rows_per_step<CPL, LOADS>();
   const int step = kWaves * (64 / LPR) * ROWS;
-  const int iters = pick_iters(g.H, step, g.n_ord);
+  const int iters = pick_iters(g.H, step, g.n_ord, size_t(step) * row_bytes<WD>(g.I), MOE_GEMV_WG_BYTES_DN);
   dim3 grid((g.H + step * iters - 1) / (step * iters), g.n_ord), block(kThreads);
   const size_t lds = size_t(kTokL) * g.I * 4;
   if (lds > 65536) {

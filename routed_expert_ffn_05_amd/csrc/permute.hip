@@ -546,6 +546,8 @@ hipError_t launch_route_permute(const float* logits, const float* bias, int T, i
     return launch_rp<2>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);
   if (vpl <= 4)
     return launch_rp<4>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);
+  if (vpl <= 6)
+    return launch_rp<6>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);
   if (vpl <= 8)
     return launch_rp<8>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);
   return launch_rp<16>(logits, bias, T, k, E, score, renorm, idx, w, slot_map, S, counts, off, perm, inv, mc, mt, me, mw, err, st);

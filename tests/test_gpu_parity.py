@@ -232,3 +232,52 @@ def test_exact_ties_resolved_by_expert_id(T):
     res = g.route_permute()
     assert np.array_equal(res["topk_idx"], ref["topk_idx"])
     np.testing.assert_allclose(res["topk_w"], ref["topk_w"], rtol=1e-6)
+
+
+def _near_tie_logits(T, E, rng):
+    """Per token: background logits in [-2, 0) and a cluster of values a few float steps apart
+    near 1.0 (0.25 for every fourth token), placed on random experts.  The cluster spans 600
+    float steps, so its members often agree in all but the last 9 bits, with a few exact ties;
+    the selection must still follow the exact logits (then the lower expert id)."""
+    lg = (-2.0 * rng.random((T, E))).astype(np.float32)
+    for t in range(T):
+        base = np.float32(1.0 if t % 4 else 0.25)
+        n = int(rng.integers(2, 14))
+        steps = rng.integers(0, 600, n)
+        if t % 3 == 0:
+            steps[1] = steps[0]                    # one exact tie
+        e = rng.choice(E, n, replace=False)
+        vals = np.full(n, base, np.float32).view(np.uint32) + steps.astype(np.uint32)
+        lg[t, e] = vals.view(np.float32)
+        if t % 5 == 1:                             # seven clear winners above a near-tied 8th place
+            lg[t, rng.choice(np.setdiff1d(np.arange(E), e), 7, replace=False)] = 3.0 + np.arange(7, dtype=np.float32)
+    return lg
+
+
+@pytest.mark.parametrize("name,T,E,k", [("decode_bf16", 4, 384, 8), ("decode_fp8", 37, 384, 8),
+                                        ("decode_fp8", 3, 200, 4), ("compact_mxfp4", 1, 384, 8),
+                                        ("decode_fp8", 2, 500, 8)])
+def test_near_ties_select_by_exact_logit(name, T, E, k):
+    # logits that agree in all but their last bits: the router's top-k, the fused top-k and
+    # permutation, and (T <= 4) the two-launch decode layer must all select and order the experts
+    # exactly as the oracle does
+    _gpu()
+    import routed_expert_ffn_05_amd as moe
+    from gpu_cases import GpuCase, run_oracle
+    cfg = gen.config(name, T=T, H=256, E=E, I=128, k=k, router="uniform",
+                     **({"resident": min(E, 120)} if name == "compact_mxfp4" else {}))
+    inp = gen.make_inputs(cfg)
+    inp.logits = _near_tie_logits(T, E, np.random.default_rng(1000 + T + E))
+    _banner(f"near-ties/{name}/T{T}/E{E}/k{k}", cfg)
+    g = GpuCase(inp)
+    ref = run_oracle(inp)
+    idx, w, _ = g.route()
+    assert np.array_equal(idx, ref["topk_idx"]), "router top-k"
+    np.testing.assert_allclose(w, ref["topk_w"], rtol=1e-6)
+    res = g.route_permute()
+    assert np.array_equal(res["topk_idx"], ref["topk_idx"]), "route + permute top-k"
+    assert np.array_equal(res["topk_w"].view(np.uint32), w.view(np.uint32))
+    if T <= 4:
+        lay = g.layer(path=moe.MOE_PATH_GEMV, mode=moe.MOE_MODE_A)
+        assert np.array_equal(lay["topk_idx"].reshape(T, k), ref["topk_idx"]), "decode layer top-k"
+        assert np.array_equal(lay["topk_w"].reshape(T, k).view(np.uint32), w.view(np.uint32))

@@ -151,6 +151,8 @@ hipError_t launch_topk(const float* logits, const float* bias, int add_bias, int
     topk_kernel<2><<<grid, block, 0, st>>>(logits, bias, add_bias, T, E, k, score, renorm, idx, w);
   else if (vpl <= 4)
     topk_kernel<4><<<grid, block, 0, st>>>(logits, bias, add_bias, T, E, k, score, renorm, idx, w);
+  else if (vpl <= 6)
+    topk_kernel<6><<<grid, block, 0, st>>>(logits, bias, add_bias, T, E, k, score, renorm, idx, w);
   else if (vpl <= 8)
     topk_kernel<8><<<grid, block, 0, st>>>(logits, bias, add_bias, T, E, k, score, renorm, idx, w);
   else

@@ -9,9 +9,10 @@ namespace moe {
 // id, so short keys are distinct and ordered by (rounded-down logit, id).  Each lane sorts its
 // short keys, then sorted lists of 8 are merged across lanes: two sorted lists A and B
 // (descending) give their 8 largest keys as the bitonic sequence max(A[i], B[7 - i]), sorted by
-// three half-cleaner levels.  Six merges with partners at lane distance 1, 2, 4, 8 (in-row DPP
-// permutations), 16 and 32 (row and half-wave swaps) leave the wave's 8 largest short keys, in
-// order, in every lane.  Rounding down never reverses two logits, only merges them, so the list
+// three half-cleaner levels.  Six merges, each with a partner lane in the other half of an
+// aligned group of 2, 4, 8, 16, 32 and 64 lanes (DPP quad permutations, the half-row and row
+// mirrors, then the row and half-wave swaps), leave the wave's 8 largest short keys, in order, in
+// every lane.  Rounding down never reverses two logits, only merges them, so the list
 // is the exact selection in the exact order when no two of its entries share a rounded logit and
 // no value outside it shares the last entry's; otherwise the exact rounds decide.
 constexpr uint32_t kShortIdBits = 9;
@@ -91,8 +92,8 @@ __device__ __forceinline__ void wave_top8_short(const uint32_t (&key)[VPL], uint
 #pragma unroll
   for (int i = 0; i < 8; ++i) c[i] = i < VPL ? key[i] : 0u;
   skey_sort8(c);
-  skey_merge_dpp<0xB1>(c);   // quad_perm [1,0,3,2]: lane distance 1
-  skey_merge_dpp<0x4E>(c);   // quad_perm [2,3,0,1]: distance 2
+  skey_merge_dpp<0xB1>(c);   // quad_perm [1,0,3,2]: the other lane of each pair
+  skey_merge_dpp<0x4E>(c);   // quad_perm [2,3,0,1]: the other pair of each quad
   skey_merge_dpp<0x141>(c);  // row_half_mirror: the other quad of each 8 lanes
   skey_merge_dpp<0x140>(c);  // row_mirror: the other 8 lanes of each row
   skey_merge_swap<16>(c);

@@ -897,7 +897,8 @@ def main(argv=None):
         summarize_mfma(a.summarize_mfma, a.out, " ".join(a.command))
         return 0
     if a.summarize_pmc:
-        cmds = " ".join(a.command).split(" ;; ")
+        # the two commands as two arguments, or in one joined by " ;; "
+        cmds = list(a.command) if len(a.command) == 2 else " ".join(a.command).split(" ;; ")
         summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], a.out, cmds[0], cmds[-1], a.pmc_kind,
                       a.pmc_copy_bytes, a.pmc_bytes_per_launch)
         return 0

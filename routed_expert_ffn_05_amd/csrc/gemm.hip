@@ -912,11 +912,13 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
                                                                  int4* __restrict__ tiles_gu,
                                                                  int4* __restrict__ tiles_dn,
                                                                  int32_t* __restrict__ counts) {
-  extern __shared__ int32_t mbase[];  // [S + 1] M-tile bases; then useq[umax], toff[umax] (balanced)
+  // [S + 1] M-tile bases; then (balanced) useq[umax], toff[umax], and per listed M tile its slot and
+  // row count (tma) and first row (tmr)
+  extern __shared__ int32_t mbase[];
   __shared__ int32_t wsum[kSchedWaves];
   __shared__ int32_t wkey[kSchedWaves][kKeys];  // per-wave key counts, then their bases
   __shared__ int32_t kbase[kKeys];
-  __shared__ int32_t xcnt[8];
+  __shared__ int32_t xcnt[8], xbase[9];
   __shared__ int32_t nunits, balanced;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int cap_gu = slots_gu >> 3, cap_dn = slots_dn >> 3;
@@ -1000,6 +1002,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   if (balanced) {
     int32_t* useq = mbase + S + 1;  // sorted units: (unit index << 10) | slot
     int32_t* toff = useq + umax;    // M-tile offset of a unit in its XCD's list
+    int32_t* tma = toff + umax;     // listed M tile (XCD x's M tiles from xbase[x]): slot | rows << 16
+    int32_t* tmr = tma + umax;      // its first row
     if (tid < S) {
       const int nf = nu - (ksmall >= 0 ? 1 : 0);
       for (int i = 0; i < nf; ++i) useq[fb + i] = (i << 10) | tid;
@@ -1044,18 +1048,40 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
     }
     __syncthreads();
     if (balanced) {
+      if (tid == 0) {
+        int run = 0;
+        for (int x = 0; x < 8; ++x) {
+          xbase[x] = run;
+          run += xcnt[x];
+        }
+        xbase[8] = run;
+      }
+      __syncthreads();
+      // every listed M tile: slot, rows, first row (a unit's M tiles are consecutive in its list)
       for (int i = tid; i < U; i += kSchedThreads) {
         const int q = useq[i], s = q & 1023, m0 = kUnitM * (q >> 10);
         const int mu = min(kUnitM, (mbase[s + 1] - mbase[s]) - m0);
-        const int x = serp_xcd(i);
         const int lo = min(max(off[s], 0), cap), hi = min(max(off[s + 1], lo), cap);
-        for (int g = 0; g < 2; ++g) {
-          const int NT = g ? nt_dn : nt_gu;
-          int4* tl = (g ? tiles_dn : tiles_gu) + size_t(x) * (g ? cap_dn : cap_gu) + size_t(toff[i]) * NT;
-          for (int mm = 0; mm < mu; ++mm) {
-            const int r0 = lo + (m0 + mm) * BM;
-            for (int n = 0; n < NT; ++n) tl[mm * NT + n] = make_int4(s, r0, min(BM, hi - r0), n);
-          }
+        const int b = xbase[serp_xcd(i)] + toff[i];
+        for (int mm = 0; mm < mu; ++mm) {
+          const int r0 = lo + (m0 + mm) * BM;
+          tma[b + mm] = s | (min(BM, hi - r0) << 16);
+          tmr[b + mm] = r0;
+        }
+      }
+      __syncthreads();
+      // the lists, written in order (consecutive threads, consecutive entries): entry j of XCD x is
+      // N tile j % NT of listed M tile j / NT
+      for (int g = 0; g < 2; ++g) {
+        const int NT = g ? nt_dn : nt_gu;
+        int4* tl = g ? tiles_dn : tiles_gu;
+        const size_t cx = g ? cap_dn : cap_gu;
+        for (int e = tid; e < xbase[8] * NT; e += kSchedThreads) {
+          int x = 0;
+          while (x < 7 && e >= xbase[x + 1] * NT) ++x;
+          const int j = e - xbase[x] * NT, m = j / NT;
+          const int a = tma[xbase[x] + m];
+          tl[size_t(x) * cx + j] = make_int4(a & 0xFFFF, tmr[xbase[x] + m], a >> 16, j - m * NT);
         }
       }
       if (tid < 8) {
@@ -1118,14 +1144,14 @@ int gemm_nt_down(int H) { return (H + gemm::BN - 1) / gemm::BN; }
 
 hipError_t launch_gemm_schedule(const GemmArgs& g, hipStream_t st) {
   const int ngu = gemm_nt_gate_up(g.I), ndn = gemm_nt_down(g.H);
-  // the balanced order keeps two words per unit in LDS (units <= M tiles <= the bound below);
-  // beyond the LDS budget the scheduler falls back to contiguous runs
+  // the balanced order keeps two words per unit and two per M tile in LDS (units <= M tiles <= the
+  // bound below); beyond the LDS budget the scheduler falls back to contiguous runs
   constexpr size_t kDynLdsMax = 150 * 1024;
   const size_t base = sizeof(int32_t) * size_t(g.S + 1);
   const size_t umax = gemm_tiles_max(g.T, g.k, g.S, 1);
   // the caller may ask for the fallback order (same results, other placement)
-  const bool fits = !g.tiles_contiguous && base + 2 * sizeof(int32_t) * umax <= kDynLdsMax;
-  const size_t lds = fits ? base + 2 * sizeof(int32_t) * umax : base;
+  const bool fits = !g.tiles_contiguous && base + 4 * sizeof(int32_t) * umax <= kDynLdsMax;
+  const size_t lds = fits ? base + 4 * sizeof(int32_t) * umax : base;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm::schedule_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));

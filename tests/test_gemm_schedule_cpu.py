@@ -66,7 +66,7 @@ def schedule(counts, cap, nt_gu, nt_dn):
                 useq.append((nu[s] - 1, s))
                 keyq.append(key)
     U = len(useq)
-    need = 4 * (S + 1) + 4 * (2 * umax)
+    need = 4 * (S + 1) + 4 * (4 * umax)  # slot bases; per unit two words, per M tile two
     if not (umax > 0 and U <= umax and need <= LDS_MAX):
         return "fallback", None
     cap_gu, cap_dn = tile_slots(cap, S, nt_gu) // 8, tile_slots(cap, S, nt_dn) // 8

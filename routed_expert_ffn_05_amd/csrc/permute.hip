@@ -417,14 +417,20 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(int32_t* __rest
     }
   }
   __syncthreads();
-  // group bases per key, groups in row order
+  // group bases per key, groups in row order; eight groups' counts are read before any of their
+  // bases is written (each key's column belongs to one thread), so a column takes ngroups / 8
+  // round trips rather than one per group
   for (int key = tid; key < K1; key += kPermThreads) {
     int run = key == S ? 0 : tot[key];
-    for (int g = 0; g < ngroups; ++g) {
-      int32_t* c = table + size_t(g) * stride + key;
-      const int v = *c;
-      *c = run;
-      run += v;
+    for (int g0 = 0; g0 < ngroups; g0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = g0 + u < ngroups ? table[size_t(g0 + u) * stride + key] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (g0 + u < ngroups) table[size_t(g0 + u) * stride + key] = run;
+        run += v[u];
+      }
     }
   }
   for (int i = tid; i < S; i += kPermThreads) slot_offsets[i] = tot[i];

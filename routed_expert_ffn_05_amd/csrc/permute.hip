@@ -53,17 +53,14 @@ __device__ __forceinline__ int row_key(const int32_t* topk_idx, int E, const int
   return s < 0 ? S : s;
 }
 
-// Stable scatter of rows [c0, c0+64) of one wave given its per-key running bases wbase[key]
-// (advanced past the chunk's rows): rows sharing a key are ranked by lane order.
-__device__ __forceinline__ void scatter_chunk(const int32_t* topk_idx, const float* topk_w, int k, int E,
-                                              const int32_t* __restrict__ slot_map, int S, int c0, int r1,
-                                              int32_t* wbase, int32_t* __restrict__ perm,
-                                              int32_t* __restrict__ inv_perm, int32_t* __restrict__ miss_token,
-                                              int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight) {
+// Stable scatter of one wave's 64 rows given its per-key running bases wbase[key] (advanced past
+// the rows): rows sharing a key are ranked by lane order.  Lane l places row r = (the wave's first
+// row) + l, whose key and expert it holds (key -1 for rows past r1 or invalid rows).
+__device__ __forceinline__ void scatter_rows(int key, int e, int r, int r1, const float* topk_w, int k, int S,
+                                             int32_t* wbase, int32_t* __restrict__ perm,
+                                             int32_t* __restrict__ inv_perm, int32_t* __restrict__ miss_token,
+                                             int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight) {
   const int lane = threadIdx.x & 63;
-  const int r = c0 + lane;
-  int e = 0, key = -1;
-  if (r < r1) key = row_key(topk_idx, E, slot_map, S, r, e);
   unsigned long long todo = __ballot(key >= 0);
   int pos = -1;
   while (todo) {
@@ -88,6 +85,18 @@ __device__ __forceinline__ void scatter_chunk(const int32_t* topk_idx, const flo
       miss_weight[pos] = topk_w[r];
     }
   }
+}
+
+// the same for rows [c0, c0+64), their keys read here
+__device__ __forceinline__ void scatter_chunk(const int32_t* topk_idx, const float* topk_w, int k, int E,
+                                              const int32_t* __restrict__ slot_map, int S, int c0, int r1,
+                                              int32_t* wbase, int32_t* __restrict__ perm,
+                                              int32_t* __restrict__ inv_perm, int32_t* __restrict__ miss_token,
+                                              int32_t* __restrict__ miss_expert, float* __restrict__ miss_weight) {
+  const int r = c0 + (threadIdx.x & 63);
+  int e = 0, key = -1;
+  if (r < r1) key = row_key(topk_idx, E, slot_map, S, r, e);
+  scatter_rows(key, e, r, r1, topk_w, k, S, wbase, perm, inv_perm, miss_token, miss_expert, miss_weight);
 }
 
 __device__ void permute_body(const int32_t* topk_idx, const float* topk_w, int T, int k, int E,
@@ -456,9 +465,9 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
   __syncthreads();
   const int r0 = blockIdx.x * kPermThreads, r1 = min(R, r0 + kPermThreads);
   const int r = r0 + tid;
+  int e = 0, key = -1;  // kept for the scatter: this thread's lane places row r there too
   if (r < r1) {
-    int e;
-    const int key = row_key(topk_idx, E, slot_map, S, r, e);
+    key = row_key(topk_idx, E, slot_map, S, r, e);
     if (key >= 0) atomicAdd(&cnt[wid * K1 + key], 1);
   }
   __syncthreads();
@@ -472,10 +481,8 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
     }
   }
   __syncthreads();
-  const int c0 = r0 + wid * 64;
-  if (c0 < r1)
-    scatter_chunk(topk_idx, topk_w, k, E, slot_map, S, c0, r1, cnt + wid * K1, perm, inv_perm, miss_token,
-                  miss_expert, miss_weight);
+  if (r0 + wid * 64 < r1)
+    scatter_rows(key, e, r, r1, topk_w, k, S, cnt + wid * K1, perm, inv_perm, miss_token, miss_expert, miss_weight);
 }
 
 size_t permute_scratch_bytes(int T, int k, int E, int S) {
